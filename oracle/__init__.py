@@ -1,0 +1,227 @@
+"""fp64 CPU oracle for single-query softmax attention and the LSE merge.
+
+TEST INFRASTRUCTURE ONLY: this package is imported by ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` and by
+nothing else.  The HIP library never imports, links or calls it, and it
+imports nothing from the HIP library.  Inputs come from the shared seeded
+generator (``workloads``), which holds no attention arithmetic.
+
+Pieces:
+
+* ``attention``  -- the plain definition in C (fp64, OpenMP over independent
+  (batch, head) rows): ``softmax(scale * q.K^T) V`` and its natural-log LSE.
+  Sources: FlashDecoding++ post (TechKnowGenie), §1 (decode step) and §5
+  (unsplit ground truth as matmul, softmax, matmul).
+* ``split_attention`` -- the two-phase split form in the order of §3 of the
+  same post (per-chunk max/sum/unnormalised output, then global max,
+  correction factors, global sum, division).  Used only to pin that the
+  split is exact.
+* ``merge`` -- the LSE / online-softmax merge of two attention states that
+  the SGLang Diffusion "Parallelism Overview" page relies on for ring hops and
+  tail parts ("What happens to the shapes", "Constraints").
+* ``round_to_bf16`` -- fp64 to bfloat16, round-to-nearest-even, directly from
+  fp64 (no fp32 step), for the bf16-output tolerance.
+* ``attention_fsum_textbook`` -- pure-Python brute force with ``math.fsum``
+  and the textbook softmax (no max shift), for tiny inputs.
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed
+forms, invariants, brute force and the pages' own equivalence check.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import struct
+import subprocess
+from typing import Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "das_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libdas_oracle.so")
+_lib = None
+
+
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the C oracle with gcc (host only, no GPU code)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", src, "-o", out + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check_inputs(q, k, v, seq_lens):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if q.ndim != 3 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,D]; k, v must be [B,Hkv,Smax,D]")
+    B, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D or seq_lens.shape != (B,):
+        raise ValueError("shape mismatch between q, k/v and seq_lens")
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return q, k, v, seq_lens
+
+
+class OracleLib:
+    """ctypes view of one build of ``das_oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        p = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.das_oracle_attention.argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
+                                             ctypes.c_double, p, p]
+        lib.das_oracle_attention.restype = None
+        lib.das_oracle_split_attention.argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
+                                                   ctypes.c_double, i32, p, p]
+        lib.das_oracle_split_attention.restype = None
+        lib.das_oracle_merge.argtypes = [p, p, p, p, ctypes.c_int64, i32, p, p]
+        lib.das_oracle_merge.restype = None
+        lib.das_oracle_max_threads.argtypes = []
+        lib.das_oracle_max_threads.restype = ctypes.c_int
+        lib.das_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.das_oracle_set_threads.restype = None
+        self.lib = lib
+        self.path = path
+
+    def max_threads(self) -> int:
+        return int(self.lib.das_oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        self.lib.das_oracle_set_threads(int(n))
+
+    def attention(self, q, k, v, seq_lens, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+        """Unsplit fp64 attention.  Inputs are bf16 bit arrays (uint16)."""
+        q, k, v, seq_lens = _check_inputs(q, k, v, seq_lens)
+        B, Hq, D = q.shape
+        Hkv, smax = k.shape[1], k.shape[2]
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        self.lib.das_oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), B, Hq, Hkv,
+                                      smax, D, float(scale), _ptr(out), _ptr(lse))
+        return out, lse
+
+    def split_attention(self, q, k, v, seq_lens, scale: float,
+                        chunk: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Two-phase split form with fixed chunks of ``chunk`` rows over [0, Smax)."""
+        if chunk < 1:
+            raise ValueError("chunk must be >= 1")
+        q, k, v, seq_lens = _check_inputs(q, k, v, seq_lens)
+        B, Hq, D = q.shape
+        Hkv, smax = k.shape[1], k.shape[2]
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        self.lib.das_oracle_split_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), B, Hq,
+                                            Hkv, smax, D, float(scale), int(chunk), _ptr(out),
+                                            _ptr(lse))
+        return out, lse
+
+    def merge(self, o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
+        """LSE merge of two states; o_* are [..., D], lse_* are [...]."""
+        o_a = np.ascontiguousarray(o_a, dtype=np.float64)
+        o_b = np.ascontiguousarray(o_b, dtype=np.float64)
+        lse_a = np.ascontiguousarray(lse_a, dtype=np.float64)
+        lse_b = np.ascontiguousarray(lse_b, dtype=np.float64)
+        if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or o_a.shape[:-1] != lse_a.shape:
+            raise ValueError("merge: shape mismatch")
+        D = o_a.shape[-1]
+        rows = int(np.prod(lse_a.shape, dtype=np.int64))
+        o = np.empty_like(o_a)
+        lse = np.empty_like(lse_a)
+        self.lib.das_oracle_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), rows, D,
+                                  _ptr(o), _ptr(lse))
+        return o, lse
+
+
+def default() -> OracleLib:
+    """The oracle built from ``das_oracle.c`` (compiled on first use if missing or stale)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = OracleLib(_LIB_PATH)
+    return _lib
+
+
+def attention(q, k, v, seq_lens, scale: float):
+    return default().attention(q, k, v, seq_lens, scale)
+
+
+def split_attention(q, k, v, seq_lens, scale: float, chunk: int):
+    return default().split_attention(q, k, v, seq_lens, scale, chunk)
+
+
+def merge(o_a, lse_a, o_b, lse_b):
+    return default().merge(o_a, lse_a, o_b, lse_b)
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def set_threads(n: int) -> None:
+    default().set_threads(n)
+
+
+# ---------------------------------------------------------------------------
+# fp64 -> bfloat16, round to nearest, ties to even, straight from fp64.
+# bfloat16 keeps 8 significant bits and fp32's exponent range: normal numbers
+# down to 2^-126, subnormals spaced 2^-133, largest finite (2 - 2^-7) * 2^127.
+# ---------------------------------------------------------------------------
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Return the bfloat16 value nearest to each fp64 value (ties to even), as fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    mant, expo = np.frexp(x)                    # x = mant * 2**expo, 0.5 <= |mant| < 1
+    quantum_exp = np.maximum(expo - 8, -133)     # 8 significant bits; subnormal floor
+    scaled = np.ldexp(x, -quantum_exp)
+    r = np.ldexp(np.rint(scaled), quantum_exp)   # np.rint rounds half to even
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def bf16_bits_of(values) -> np.ndarray:
+    """Bit patterns of values that are already exactly representable in bfloat16."""
+    f = np.asarray(values, dtype=np.float64).astype(np.float32)
+    bits = f.view(np.uint32)
+    if np.any(bits & np.uint32(0xFFFF)):
+        raise ValueError("value not representable in bfloat16")
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python brute force (tiny inputs only).
+# ---------------------------------------------------------------------------
+def bf16_to_float(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def attention_fsum_textbook(q_row: Sequence[float], k_rows: Sequence[Sequence[float]],
+                            v_rows: Sequence[Sequence[float]], scale: float):
+    """Textbook softmax attention for one query row, without the max shift.
+
+    weights_j = exp(s_j) / sum_i exp(s_i);  out = sum_j weights_j v_j;
+    lse = ln sum_j exp(s_j).  Every sum is a correctly rounded ``math.fsum``.
+    Valid only while exp(s_j) stays finite.
+    """
+    s = [scale * math.fsum(a * b for a, b in zip(q_row, k)) for k in k_rows]
+    e = [math.exp(x) for x in s]
+    Z = math.fsum(e)
+    D = len(v_rows[0]) if v_rows else len(q_row)
+    out = [math.fsum(e[j] * v_rows[j][d] for j in range(len(e))) / Z for d in range(D)]
+    return out, math.log(Z)

@@ -1,0 +1,232 @@
+/*
+ * das_oracle.c -- fp64 CPU oracle for single-query (decode) softmax attention
+ * and the log-sum-exp merge of attention states.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; it includes nothing but libc,
+ * libm and OpenMP.
+ *
+ * Sources (cited by page title and section):
+ *   [FD++]  "FlashDecoding++: 시퀀스 차원 KV 분할 병렬화와 GPU 언더유틸라이제이션
+ *           극복을 통한 LLM 서빙 극대화" (TechKnowGenie post).  §1 describes the
+ *           decode step (one query token against N cached K/V rows); §3
+ *           describes phase 1 (per-chunk logits, chunk max, exponentials,
+ *           chunk sum, unnormalised chunk output) and phase 2 (global max,
+ *           per-chunk correction factors, global sum, final division); §5
+ *           computes the unsplit ground truth as matmul -> softmax -> matmul.
+ *   [SGL-PAR] "병렬 처리 개요 (Parallelism Overview)", SGLang Diffusion docs
+ *           (data-sketchers wiki).  "What happens to the shapes" and
+ *           "Constraints": ring attention and the tail/replicated-part path
+ *           join partial attention results through an online-softmax merge
+ *           that needs each part's softmax log-sum-exp.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   - lse is the natural log of the sum of exp(scaled logit);
+ *   - no epsilon is added to the softmax denominator (the emulator in §5 adds
+ *     one, but the pages call the result exact, and the denominator is >= 1);
+ *   - GQA: query head h reads kv-head h / (Hq / Hkv);
+ *   - seq_lens[b] is clamped to [0, Smax]; an empty row set gives out = 0,
+ *     lse = -inf (the identity of the merge);
+ *   - scale multiplies the finished dot product q.k.
+ *
+ * Arithmetic: every bf16 input is widened exactly to double; dot products,
+ * exponentials, sums and divisions run in double with libm exp/log, in the
+ * plain order the definition states.  Build with -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double widen_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static int clamp_len(int32_t L, int32_t smax) {
+  if (L < 0) return 0;
+  if (L > smax) return smax;
+  return L;
+}
+
+int das_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void das_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* Logit of row j for query row qrow: scale * sum_d q[d] * k[j][d]. */
+static double logit(const uint16_t* qrow, const uint16_t* krow, int D, double scale) {
+  double dot = 0.0;
+  for (int d = 0; d < D; ++d) dot += widen_bf16(qrow[d]) * widen_bf16(krow[d]);
+  return scale * dot;
+}
+
+/*
+ * Unsplit attention, the plain definition ([FD++] §1 decode step, §5 ground
+ * truth):  s_j = scale * q.k_j,  M = max_j s_j,  w_j = exp(s_j - M),
+ * Z = sum_j w_j,  out = sum_j w_j v_j / Z,  lse = M + ln Z.
+ *
+ * q: [B][Hq][D] bf16 bits; k, v: [B][Hkv][Smax][D] bf16 bits;
+ * out: [B][Hq][D] double; lse: [B][Hq] double.
+ */
+void das_oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / G;
+      const int L = clamp_len(seq_lens[b], Smax);
+      const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
+      const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      double* o = out + ((size_t)b * Hq + h) * D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (L == 0) {
+        lse[(size_t)b * Hq + h] = -INFINITY;
+        continue;
+      }
+      double* w = (double*)malloc(sizeof(double) * (size_t)L);
+      double M = -INFINITY;
+      for (int j = 0; j < L; ++j) {
+        w[j] = logit(qrow, kbase + (size_t)j * D, D, scale);
+        if (w[j] > M) M = w[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j < L; ++j) {
+        w[j] = exp(w[j] - M);
+        Z += w[j];
+      }
+      for (int j = 0; j < L; ++j) {
+        const uint16_t* vrow = vbase + (size_t)j * D;
+        for (int d = 0; d < D; ++d) o[d] += w[j] * widen_bf16(vrow[d]);
+      }
+      for (int d = 0; d < D; ++d) o[d] /= Z;
+      lse[(size_t)b * Hq + h] = M + log(Z);
+      free(w);
+    }
+  }
+}
+
+/*
+ * Two-phase split form, in the order [FD++] §3 gives it.  The row range
+ * [0, Smax) is cut into consecutive chunks of `chunk` rows (the last one
+ * ragged); rows at or past seq_lens[b] belong to no chunk, so trailing chunks
+ * can be empty.
+ *   Phase 1, per chunk c: logits over the chunk, chunk max m_c, exponentials
+ *     p_j = exp(s_j - m_c), chunk sum l_c = sum p_j, unnormalised output
+ *     o_c = sum p_j v_j.  An empty chunk has m_c = -inf, l_c = 0, o_c = 0.
+ *   Phase 2: global max M = max_c m_c, factor f_c = exp(m_c - M) (0 for an
+ *     empty chunk), global sum Lsum = sum_c f_c l_c, output
+ *     out = (sum_c f_c o_c) / Lsum, and lse = M + ln Lsum.
+ * Used to pin that splitting is exact; the GPU path is never compared to it.
+ */
+void das_oracle_split_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t Smax, int32_t D, double scale, int32_t chunk,
+                                double* out, double* lse) {
+  const int G = Hq / Hkv;
+  const int nchunks = chunk > 0 ? (Smax + chunk - 1) / chunk : 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / G;
+      const int L = clamp_len(seq_lens[b], Smax);
+      const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
+      const uint16_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      const uint16_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      double* o = out + ((size_t)b * Hq + h) * D;
+      double* m_c = (double*)malloc(sizeof(double) * (size_t)(nchunks > 0 ? nchunks : 1));
+      double* l_c = (double*)malloc(sizeof(double) * (size_t)(nchunks > 0 ? nchunks : 1));
+      double* o_c = (double*)calloc((size_t)(nchunks > 0 ? nchunks : 1) * D, sizeof(double));
+      double* p = (double*)malloc(sizeof(double) * (size_t)(chunk > 0 ? chunk : 1));
+      /* phase 1 */
+      for (int c = 0; c < nchunks; ++c) {
+        const int j0 = c * chunk;
+        const int j1 = (j0 + chunk < L) ? j0 + chunk : L;
+        m_c[c] = -INFINITY;
+        l_c[c] = 0.0;
+        if (j1 <= j0) continue;
+        for (int j = j0; j < j1; ++j) {
+          p[j - j0] = logit(qrow, kbase + (size_t)j * D, D, scale);
+          if (p[j - j0] > m_c[c]) m_c[c] = p[j - j0];
+        }
+        for (int j = j0; j < j1; ++j) {
+          p[j - j0] = exp(p[j - j0] - m_c[c]);
+          l_c[c] += p[j - j0];
+        }
+        for (int j = j0; j < j1; ++j) {
+          const uint16_t* vrow = vbase + (size_t)j * D;
+          for (int d = 0; d < D; ++d) o_c[(size_t)c * D + d] += p[j - j0] * widen_bf16(vrow[d]);
+        }
+      }
+      /* phase 2 */
+      double M = -INFINITY;
+      for (int c = 0; c < nchunks; ++c)
+        if (m_c[c] > M) M = m_c[c];
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (M == -INFINITY) {
+        lse[(size_t)b * Hq + h] = -INFINITY;
+      } else {
+        double Lsum = 0.0;
+        for (int c = 0; c < nchunks; ++c) {
+          const double f = (m_c[c] == -INFINITY) ? 0.0 : exp(m_c[c] - M);
+          Lsum += f * l_c[c];
+          for (int d = 0; d < D; ++d) o[d] += f * o_c[(size_t)c * D + d];
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Lsum;
+        lse[(size_t)b * Hq + h] = M + log(Lsum);
+      }
+      free(m_c);
+      free(l_c);
+      free(o_c);
+      free(p);
+    }
+  }
+}
+
+/*
+ * Merge of two normalised attention states over disjoint row sets
+ * ([SGL-PAR] "What happens to the shapes", "Constraints": online-softmax
+ * merge driven by each part's LSE):
+ *   mx = max(a, b); if mx = -inf the result is (0, -inf);
+ *   lse = mx + ln(exp(a - mx) + exp(b - mx));
+ *   o = exp(a - lse) o_a + exp(b - lse) o_b.
+ * The formula is symmetric in its two arguments.
+ */
+void das_oracle_merge(const double* o_a, const double* lse_a, const double* o_b,
+                      const double* lse_b, int64_t rows, int32_t D, double* o_out,
+                      double* lse_out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const double a = lse_a[r], b = lse_b[r];
+    const double mx = a > b ? a : b;
+    double* o = o_out + (size_t)r * D;
+    if (mx == -INFINITY) {
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      lse_out[r] = -INFINITY;
+      continue;
+    }
+    const double lse = mx + log(exp(a - mx) + exp(b - mx));
+    const double wa = exp(a - lse), wb = exp(b - lse);
+    for (int d = 0; d < D; ++d) o[d] = wa * o_a[(size_t)r * D + d] + wb * o_b[(size_t)r * D + d];
+    lse_out[r] = lse;
+  }
+}

@@ -1,0 +1,343 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes one build of the oracle (``oracle.OracleLib``)
+and raises ``AssertionError`` when that build disagrees with a closed form, an
+invariant of softmax attention or the LSE merge, a pure-Python brute force, a
+library routine, or the equivalence check printed in the FlashDecoding++ post
+(TechKnowGenie, §5).  ``tests/test_oracle.py`` runs them on the real oracle;
+``tests/test_oracle_mutants.py`` runs them on copies of the oracle with planted
+mistakes and requires every mistake to be caught.
+"""
+from __future__ import annotations
+
+import functools
+import json
+import math
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _bits(values) -> np.ndarray:
+    return oracle.bf16_bits_of(np.asarray(values, dtype=np.float64))
+
+
+def _f(bits) -> np.ndarray:
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _small(seed, B=2, Hq=4, Hkv=2, D=16, smax=24, lens=(24, 13), k_mult=1.0):
+    cfg = workloads.custom_config(B, Hq, Hkv, D, smax, k_mult=k_mult)
+    return workloads.make_inputs(cfg, seed, smax=smax, seq_lens=lens)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max |diff| {err:.3e} > {tol:.1e}"
+
+
+def expr(s: str):
+    """Closed-form expression from the golden files: integer, a/b, or log(n)."""
+    s = str(s).strip()
+    if re.fullmatch(r"-?\d+(/\d+)?", s):
+        return float(Fraction(s))
+    m = re.fullmatch(r"log\((\d+)\)", s)
+    if m:
+        return math.log(int(m.group(1)))
+    raise ValueError(f"unknown expression {s!r}")
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def pin_zero_query_gives_mean(lib):
+    """q = 0: every logit is 0, out = mean of the valid V rows, lse = ln L exactly."""
+    x = _small(11, lens=(24, 13))
+    q0 = np.zeros_like(x.q)
+    out, lse = lib.attention(q0, x.k, x.v, x.seq_lens, x.scale)
+    for b, L in enumerate(x.seq_lens):
+        for h in range(x.q.shape[1]):
+            g = h // (x.q.shape[1] // x.k.shape[1])
+            rows = _f(x.v[b, g, :L])
+            mean = [math.fsum(rows[:, d]) / L for d in range(rows.shape[1])]
+            _close(out[b, h], mean, 1e-14, "q=0 mean")
+            assert lse[b, h] == math.log(L), "q=0: lse must be exactly ln L"
+
+
+def pin_zero_scale_gives_mean(lib):
+    """scale = 0 with a nonzero q: same closed form as q = 0."""
+    x = _small(12, lens=(7, 24))
+    out, lse = lib.attention(x.q, x.k, x.v, x.seq_lens, 0.0)
+    for b, L in enumerate(x.seq_lens):
+        rows = _f(x.v[b, 0, :L])
+        _close(out[b, 0], rows.sum(axis=0) / L, 1e-14, "scale=0 mean")
+        assert lse[b, 0] == math.log(L)
+
+
+def pin_single_row(lib):
+    """L = 1: out is that V row exactly; lse is the logit scale * q.k_0."""
+    x = _small(13, lens=(1, 1))
+    out, lse = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    G = x.q.shape[1] // x.k.shape[1]
+    for b in range(2):
+        for h in range(x.q.shape[1]):
+            g = h // G
+            assert np.array_equal(out[b, h], _f(x.v[b, g, 0])), "L=1: out must equal the V row"
+            s = x.scale * math.fsum(_f(x.q[b, h]) * _f(x.k[b, g, 0]))
+            assert abs(lse[b, h] - s) <= 1e-15 * max(1.0, abs(s)), "L=1: lse must be the logit"
+
+
+def pin_worked_examples(lib):
+    """Hand-derived closed forms stored in tests/golden/worked_examples.json."""
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as fh:
+        doc = json.load(fh)
+    for ex in doc["examples"]:
+        Hq, Hkv, D = ex["Hq"], ex["Hkv"], ex["D"]
+        L = len(ex["k"][0])
+        q = _bits(ex["q"]).reshape(1, Hq, D)
+        k = _bits(ex["k"]).reshape(1, Hkv, L, D)
+        v = _bits(ex["v"]).reshape(1, Hkv, L, D)
+        out, lse = lib.attention(q, k, v, np.array([L], np.int32), expr(ex["scale"]))
+        want_out = np.array([[expr(e) for e in row] for row in ex["out"]])
+        want_lse = np.array([expr(e) for e in ex["lse"]])
+        _close(out[0], want_out, 1e-14, ex["name"] + " out")
+        _close(lse[0], want_lse, 1e-14, ex["name"] + " lse")
+
+
+def pin_one_hot_values_give_probabilities(lib):
+    """V rows = unit vectors: out[:L] is the probability vector itself.
+
+    Compared with the textbook softmax (no max shift, math.fsum) and with
+    torch's fp64 softmax / logsumexp (the unsplit ground truth of §5)."""
+    import torch
+
+    D, L = 16, 11
+    x = _small(14, B=1, Hq=2, Hkv=1, D=D, smax=L, lens=(L,))
+    v = np.zeros_like(x.v)
+    for j in range(L):
+        v[0, 0, j, j] = _bits([1.0])[0]
+    out, lse = lib.attention(x.q, x.k, v, x.seq_lens, x.scale)
+    for h in range(2):
+        qf, kf = _f(x.q[0, h]), _f(x.k[0, 0, :L])
+        ref, ref_lse = oracle.attention_fsum_textbook(list(qf), kf.tolist(), np.eye(L, D).tolist(),
+                                                      x.scale)
+        _close(out[0, h], ref, 1e-15, "one-hot V vs textbook softmax")
+        assert np.all(out[0, h, L:] == 0.0)
+        s = torch.tensor(kf @ qf * x.scale, dtype=torch.float64)
+        _close(out[0, h, :L], torch.softmax(s, 0).numpy(), 1e-15, "one-hot V vs torch softmax")
+        assert abs(lse[0, h] - torch.logsumexp(s, 0).item()) <= 1e-14
+        assert abs(lse[0, h] - ref_lse) <= 1e-14
+
+
+def pin_two_rows_huge_logits(lib):
+    """Two rows with logits near 1000, where exp overflows fp64 without the max shift.
+
+    Closed form: out = sigma(a-b) v0 + sigma(b-a) v1, lse = max(a,b) + log1p(exp(-|a-b|))."""
+    q = _bits([[[1, 0, 0, 0]]])
+    k = _bits([[[[1, 0, 0, 0], [1.0078125, 0, 0, 0]]]])
+    v = _bits([[[[1, -2, 0.5, 3], [-1, 4, 0.25, -3]]]])
+    scale = 1000.0
+    a, b = scale * 1.0, scale * 1.0078125
+    out, lse = lib.attention(q, k, v, np.array([2], np.int32), scale)
+    assert np.all(np.isfinite(out)) and math.isfinite(lse[0, 0])
+    sa = 1.0 / (1.0 + math.exp(b - a))
+    sb = 1.0 / (1.0 + math.exp(a - b))
+    want = sa * _f(v[0, 0, 0]) + sb * _f(v[0, 0, 1])
+    _close(out[0, 0], want, 1e-15, "two-row closed form")
+    assert abs(lse[0, 0] - (max(a, b) + math.log1p(math.exp(-abs(a - b))))) <= 1e-12
+
+
+def pin_identical_keys_give_mean(lib):
+    """All K rows equal: equal weights, out = mean V, lse = s + ln L."""
+    x = _small(15, B=1, Hq=2, Hkv=1, D=8, smax=9, lens=(9,))
+    k = np.broadcast_to(x.k[:, :, :1, :], x.k.shape).copy()
+    out, lse = lib.attention(x.q, k, x.v, x.seq_lens, x.scale)
+    rows = _f(x.v[0, 0])
+    for h in range(2):
+        _close(out[0, h], rows.mean(axis=0), 1e-15, "identical keys mean")
+        s = x.scale * math.fsum(_f(x.q[0, h]) * _f(k[0, 0, 0]))
+        assert abs(lse[0, h] - (s + math.log(9))) <= 1e-14
+
+
+def pin_gqa_head_mapping(lib):
+    """kv-head g holds constant V = 2^g: query head h must return 2^(h // G) exactly."""
+    for Hq, Hkv in ((8, 2), (8, 8), (8, 1), (6, 3)):
+        x = _small(16, B=2, Hq=Hq, Hkv=Hkv, D=4, smax=10, lens=(10, 6))
+        v = np.zeros_like(x.v)
+        for g in range(Hkv):
+            v[:, g] = _bits([2.0 ** g])[0]
+        out, _ = lib.attention(x.q, x.k, v, x.seq_lens, x.scale)
+        G = Hq // Hkv
+        for h in range(Hq):
+            assert np.all(out[:, h] == 2.0 ** (h // G)), f"head {h} of Hq={Hq}, Hkv={Hkv}"
+
+
+def pin_empty_and_poisoned_rows(lib):
+    """L = 0 gives (0, -inf); NaN rows past L never leak; L > Smax is clamped to Smax."""
+    x = _small(17, lens=(0, 5))
+    assert np.isnan(_f(x.k[1, 0, 5])).all()
+    out, lse = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    assert np.all(out[0] == 0.0) and np.all(lse[0] == -np.inf)
+    assert np.all(np.isfinite(out[1])) and np.all(np.isfinite(lse[1]))
+    y = _small(18, lens=(24, 24))
+    full = lib.attention(y.q, y.k, y.v, y.seq_lens, y.scale)
+    over = lib.attention(y.q, y.k, y.v, np.array([30, 99], np.int32), y.scale)
+    assert np.array_equal(full[0], over[0]) and np.array_equal(full[1], over[1])
+
+
+def pin_bruteforce_tiny(lib):
+    """C oracle vs the pure-Python textbook formula with math.fsum on tiny inputs."""
+    for D, lens in ((4, (40, 3)), (64, (17, 1))):
+        x = _small(19 + D, B=2, Hq=4, Hkv=2, D=D, smax=40, lens=lens)
+        out, lse = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+        for b, L in enumerate(lens):
+            for h in range(4):
+                g = h // 2
+                ref, ref_lse = oracle.attention_fsum_textbook(
+                    _f(x.q[b, h]).tolist(), _f(x.k[b, g, :L]).tolist(), _f(x.v[b, g, :L]).tolist(),
+                    x.scale)
+                _close(out[b, h], ref, 1e-13, f"brute force D={D} b={b} h={h}")
+                assert abs(lse[b, h] - ref_lse) <= 1e-13
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+def pin_row_permutation_invariance(lib):
+    """Permuting the valid K/V rows (same permutation on both) changes nothing."""
+    x = _small(20, lens=(24, 19))
+    rng = np.random.default_rng(0)
+    k, v = x.k.copy(), x.v.copy()
+    for b, L in enumerate(x.seq_lens):
+        perm = rng.permutation(L)
+        k[b, :, :L] = x.k[b, :, perm].transpose(1, 0, 2)
+        v[b, :, :L] = x.v[b, :, perm].transpose(1, 0, 2)
+    a = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    p = lib.attention(x.q, k, v, x.seq_lens, x.scale)
+    _close(a[0], p[0], 1e-14, "permuted rows out")
+    _close(a[1], p[1], 1e-13, "permuted rows lse")
+
+
+def pin_linear_in_v(lib):
+    """out(2V) = 2 out(V) exactly, and out(Va + Vb) = out(Va) + out(Vb)."""
+    x = _small(21, lens=(24, 10))
+    o1, _ = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    v2 = _bits(np.nan_to_num(_f(x.v)) * 2.0)
+    o2, _ = lib.attention(x.q, x.k, v2, x.seq_lens, x.scale)
+    assert np.array_equal(o2, 2.0 * o1), "doubling V must double out exactly"
+    rng = np.random.default_rng(1)
+    va = rng.integers(-8, 9, size=x.v.shape).astype(np.float64)
+    vb = rng.integers(-8, 9, size=x.v.shape).astype(np.float64)
+    oa, _ = lib.attention(x.q, x.k, _bits(va), x.seq_lens, x.scale)
+    ob, _ = lib.attention(x.q, x.k, _bits(vb), x.seq_lens, x.scale)
+    oab, _ = lib.attention(x.q, x.k, _bits(va + vb), x.seq_lens, x.scale)
+    _close(oab, oa + ob, 1e-13, "linearity in V")
+
+
+def pin_split_equals_unsplit(lib):
+    """The two-phase split is exact for every chunking, empty trailing chunks included."""
+    x = _small(22, B=3, Hq=8, Hkv=2, D=16, smax=40, lens=(40, 23, 1), k_mult=4.0)
+    full = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    for chunk in (1, 2, 3, 5, 16, 39, 40, 47):
+        sp = lib.split_attention(x.q, x.k, x.v, x.seq_lens, x.scale, chunk)
+        _close(sp[0], full[0], 1e-13, f"split chunk={chunk} out")
+        _close(sp[1], full[1], 1e-13, f"split chunk={chunk} lse")
+
+
+@functools.lru_cache(maxsize=1)
+def _fd_check_inputs():
+    with open(os.path.join(GOLDEN, "fd_equivalence_check.json")) as fh:
+        fix = json.load(fh)["what_the_page_fixes"]
+    cfg = workloads.custom_config(fix["batch"], fix["heads"], fix["heads"], fix["head_dim"],
+                                  fix["seq_len"])
+    return fix, workloads.make_inputs(cfg, fix["seed"])
+
+
+def pin_fd_equivalence_check(lib):
+    """The page's own check (§5): B=1, H=32, D=128, S=8192, chunk 512, |split - unsplit| < 1e-5."""
+    fix, x = _fd_check_inputs()
+    full = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    sp = lib.split_attention(x.q, x.k, x.v, x.seq_lens, x.scale, fix["chunk"])
+    err = float(np.max(np.abs(full[0] - sp[0])))
+    assert err < fix["max_abs_deviation_bound"], "the page's bound"
+    assert err < 1e-13, f"fp64 split deviates by {err:.3e}"
+    _close(sp[1], full[1], 1e-12, "fd check lse")
+
+
+def pin_merge_algebra(lib):
+    """Merge: commutative (bitwise), associative, -inf is the identity, merge(s, s) = (o, lse + ln 2)."""
+    rng = np.random.default_rng(2)
+    R, D = 7, 5
+    o = [rng.standard_normal((R, D)) for _ in range(3)]
+    s = [rng.standard_normal(R) * 20 for _ in range(3)]
+    ab = lib.merge(o[0], s[0], o[1], s[1])
+    ba = lib.merge(o[1], s[1], o[0], s[0])
+    assert np.array_equal(ab[0], ba[0]) and np.array_equal(ab[1], ba[1]), "commutativity"
+    left = lib.merge(ab[0], ab[1], o[2], s[2])
+    bc = lib.merge(o[1], s[1], o[2], s[2])
+    right = lib.merge(o[0], s[0], bc[0], bc[1])
+    _close(left[0], right[0], 1e-13, "associativity out")
+    _close(left[1], right[1], 1e-13, "associativity lse")
+    ident = lib.merge(o[0], s[0], np.zeros((R, D)), np.full(R, -np.inf))
+    _close(ident[0], o[0], 0.0, "identity out")
+    _close(ident[1], s[0], 0.0, "identity lse")
+    twice = lib.merge(o[0], s[0], o[0], s[0])
+    _close(twice[0], o[0], 1e-13, "self-merge out")
+    _close(twice[1], s[0] + math.log(2.0), 1e-14, "self-merge lse")
+    empty = lib.merge(o[0], np.full(R, -np.inf), o[1], np.full(R, -np.inf))
+    assert np.all(empty[0] == 0.0) and np.all(empty[1] == -np.inf)
+    # weights: a dominant side wins; closed form of the two-state merge
+    w = lib.merge(np.ones((1, 1)), np.array([0.0]), np.zeros((1, 1)), np.array([math.log(3.0)]))
+    _close(w[0], [[0.25]], 1e-16, "merge weights 1:3")
+    _close(w[1], [math.log(4.0)], 1e-15, "merge lse ln(1+3)")
+
+
+def pin_merge_of_halves_equals_whole(lib):
+    """Attention over rows [0, m) merged with attention over [m, L) equals attention over [0, L)."""
+    x = _small(23, B=2, Hq=4, Hkv=2, D=16, smax=30, lens=(30, 21), k_mult=4.0)
+    whole = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    for m in (1, 9, 20):
+        first = lib.attention(x.q, x.k, x.v, np.minimum(x.seq_lens, m).astype(np.int32), x.scale)
+        k2 = np.full_like(x.k, workloads.BF16_QNAN)
+        v2 = np.full_like(x.v, workloads.BF16_QNAN)
+        k2[:, :, :30 - m] = x.k[:, :, m:]
+        v2[:, :, :30 - m] = x.v[:, :, m:]
+        second = lib.attention(x.q, k2, v2, np.maximum(x.seq_lens - m, 0).astype(np.int32),
+                               x.scale)
+        merged = lib.merge(first[0], first[1], second[0], second[1])
+        _close(merged[0], whole[0], 1e-13, f"halves at {m}: out")
+        _close(merged[1], whole[1], 1e-13, f"halves at {m}: lse")
+
+
+# cheap pins first, the page-sized equivalence check last
+ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_") and callable(v)),
+                  key=lambda f: (f is pin_fd_equivalence_check, f.__name__))
+
+
+def run_all(lib_path: str) -> int:
+    """Run every pin against one build; print the first failure.  Exit code 1 if any fails."""
+    lib = oracle.OracleLib(lib_path)
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            print(f"CAUGHT {pin.__name__}: {e}", flush=True)
+            return 1
+    print("ALL PINS PASS", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    import sys
+
+    sys.exit(run_all(sys.argv[1]))

@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs for single-query split-KV decode attention.
+
+This module only draws and packs inputs. It holds none of the attention
+arithmetic, so that both the fp64 oracle (``oracle/``) and the HIP library
+(``decode_attention_split_amd``) can be fed the same bits without sharing any
+code with each other.
+
+Recipe (one config = one seed, ``seed = 42 + config index``):
+
+* ``numpy.random.Generator(PCG64(seed))``.
+* From the main stream, in this order: ``seq_lens`` (only when lengths are
+  random), then q as one float32 ``standard_normal`` draw in (batch, head, d)
+  order.
+* K and V of batch row ``b``, kv-head ``h`` come from their own stream,
+  ``PCG64(seed).jumped(1 + (t*B + b)*Hkv + h)`` with ``t = 0`` for K and
+  ``t = 1`` for V: one float32 ``standard_normal`` draw over the valid rows
+  in (row, d) order.  Independent streams let large caches be filled on
+  several host threads.
+* Every draw is rounded to bfloat16 with round-to-nearest-even.  Optional
+  exact power-of-two multipliers (the peaked-softmax stress config scales K
+  by 4) are applied after rounding.
+* K/V rows past ``seq_lens[b]`` are filled with a bfloat16 quiet NaN
+  (0x7FC0) so that any kernel reading them contaminates its result.
+* ``scale = 1/sqrt(D)`` rounded to float32 (the library takes a float).
+
+The five named configs are the decode shapes the FlashDecoding++ post
+(techknowgenie, "FlashDecoding++: 시퀀스 차원 KV 분할 병렬화 ...") argues
+about in §1-§2: single-query decode, GQA with 8 KV heads, long context, a
+batched variable-length mix and a ragged peaked-softmax stress case.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import dataclasses
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+BF16_QNAN = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    smax: int
+    seq_lens: Optional[Sequence[int]] = None   # fixed lengths; None = random or all smax
+    random_lens: Optional[tuple] = None         # (low, high) inclusive, drawn first
+    k_mult: float = 1.0                         # exact power of two applied to K after rounding
+    description: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+CONFIGS = [
+    Config("mha_b1_h8_d64_l1024", B=1, Hq=8, Hkv=8, D=64, smax=1024,
+           description="MHA decode, B=1, Hq=Hkv=8, D=64, L=1024"),
+    Config("gqa_b1_h32x8_d128_l32768", B=1, Hq=32, Hkv=8, D=128, smax=32768,
+           description="Llama-3-8B-shaped GQA decode, B=1, Hq=32, Hkv=8, D=128, L=32768"),
+    Config("gqa_b1_h32x8_d128_l131072", B=1, Hq=32, Hkv=8, D=128, smax=131072,
+           description="long-context GQA decode, B=1, Hq=32, Hkv=8, D=128, L=131072"),
+    Config("gqa_b64_h32x8_d128_varlen16k", B=64, Hq=32, Hkv=8, D=128, smax=16384,
+           random_lens=(512, 16384),
+           description="batched varlen GQA decode, B=64, L~U[512,16384], Smax=16384"),
+    Config("gqa8_b8_h64x8_d128_ragged", B=8, Hq=64, Hkv=8, D=128, smax=100003,
+           seq_lens=(1, 17, 255, 4095, 4097, 16383, 65537, 100003), k_mult=4.0,
+           description="ragged group-8 GQA stress, B=8, Hq=64, Hkv=8, K x4 (peaked softmax)"),
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 bit patterns, nearest-even (finite inputs)."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _scale_bits(bits: np.ndarray, mult: float) -> np.ndarray:
+    if mult == 1.0:
+        return bits
+    m, e = math.frexp(mult)
+    if m != 0.5:
+        raise ValueError("k_mult must be a power of two so that scaling stays exact")
+    return f32_to_bf16_bits(bf16_bits_to_f32(bits) * np.float32(mult))
+
+
+@dataclasses.dataclass
+class Inputs:
+    config: Config
+    seed: int
+    q: np.ndarray          # uint16 [B, Hq, D]
+    k: np.ndarray          # uint16 [B, Hkv, Smax, D]
+    v: np.ndarray          # uint16 [B, Hkv, Smax, D]
+    seq_lens: np.ndarray   # int32 [B]
+    scale: float
+
+    @property
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes: every valid row of K and V read once per kv-head."""
+        c = self.config
+        return int(self.seq_lens.astype(np.int64).sum()) * c.Hkv * c.D * 2 * 2
+
+
+def draw_seq_lens(cfg: Config, rng: np.random.Generator) -> np.ndarray:
+    if cfg.random_lens is not None:
+        lo, hi = cfg.random_lens
+        return rng.integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int32)
+    if cfg.seq_lens is not None:
+        return np.asarray(cfg.seq_lens, dtype=np.int32)
+    return np.full(cfg.B, cfg.smax, dtype=np.int32)
+
+
+def _fill_rows(seed: int, tensor: int, B: int, H: int, smax: int, D: int,
+               lens: np.ndarray, mult: float = 1.0) -> np.ndarray:
+    """K (tensor 0) or V (tensor 1): seeded valid rows, NaN-poisoned beyond them."""
+    out = np.full((B, H, smax, D), BF16_QNAN, dtype=np.uint16)
+
+    def one(task: int) -> None:
+        b, h = divmod(task, H)
+        L = int(lens[b])
+        if L == 0:
+            return
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(1 + (tensor * B + b) * H + h))
+        bits = f32_to_bf16_bits(rng.standard_normal(L * D, dtype=np.float32))
+        out[b, h, :L, :] = _scale_bits(bits, mult).reshape(L, D)
+
+    tasks = range(B * H)
+    workers = min(B * H, max(1, os.cpu_count() or 1), 16)
+    if workers <= 1 or B * H * int(lens.max(initial=0)) * D < (1 << 22):
+        for t in tasks:
+            one(t)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, tasks))
+    return out
+
+
+def make_inputs(cfg: Config, seed: int, smax: Optional[int] = None,
+                seq_lens: Optional[Sequence[int]] = None) -> Inputs:
+    """Draw one seeded input set for ``cfg``.
+
+    ``smax`` / ``seq_lens`` override the config's cache length and lengths
+    (used for small parity cases and edge lengths); an explicit ``seq_lens``
+    replaces the length draw.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    else:
+        lens = draw_seq_lens(cfg, rng)
+    B = len(lens)
+    S = int(smax if smax is not None else max(cfg.smax, int(lens.max(initial=0))))
+    if lens.size and (lens.min() < 0 or lens.max() > S):
+        raise ValueError("seq_lens must lie in [0, Smax]")
+    q = f32_to_bf16_bits(rng.standard_normal(B * cfg.Hq * cfg.D, dtype=np.float32))
+    q = q.reshape(B, cfg.Hq, cfg.D)
+    k = _fill_rows(seed, 0, B, cfg.Hkv, S, cfg.D, lens, cfg.k_mult)
+    v = _fill_rows(seed, 1, B, cfg.Hkv, S, cfg.D, lens)
+    return Inputs(cfg, seed, q, k, v, lens, cfg.scale)
+
+
+def config_inputs(index: int) -> Inputs:
+    """The named config ``index`` at its full size, seed 42 + index."""
+    return make_inputs(CONFIGS[index], 42 + index)
+
+
+def custom_config(B: int, Hq: int, Hkv: int, D: int, smax: int, name: str = "custom",
+                  k_mult: float = 1.0) -> Config:
+    return Config(name, B=B, Hq=Hq, Hkv=Hkv, D=D, smax=smax, k_mult=k_mult)
