@@ -1,0 +1,262 @@
+"""Thin Python binding of libdas.so (split-KV decode attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/das.h``.  PyTorch supplies
+device memory and the current HIP stream.  The functions carry the C names.
+
+If ``libdas.so`` has not been built, every call raises: there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdas.so")
+
+DAS_OK, DAS_EINVAL, DAS_ENOTSUP, DAS_EWORKSPACE, DAS_ELAUNCH = 0, -1, -2, -3, -4
+DAS_F32, DAS_BF16 = 0, 1
+DAS_MAX_SPLITS = 4096
+DAS_CHUNK_QUANTUM = 128
+DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
+
+EXPORTED = ("das_plan", "das_decode_workspace_bytes", "das_decode_attention",
+            "das_split_kv_decode", "das_lse_combine", "das_merge_attn_states", "das_strerror")
+
+_lib = None
+
+
+class DasError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {das_strerror(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdas.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(path)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.das_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, pi32, pi32]
+    lib.das_plan.restype = ctypes.c_int
+    lib.das_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.das_decode_workspace_bytes.restype = sz
+    decode_args = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_float, p, i32, p, i32, p, sz, p]
+    for name in ("das_decode_attention", "das_split_kv_decode"):
+        getattr(lib, name).argtypes = decode_args
+        getattr(lib, name).restype = ctypes.c_int
+    lib.das_lse_combine.argtypes = [p, i32, i32, i32, i32, i32, i32, p, sz, p, i32, p, p]
+    lib.das_lse_combine.restype = ctypes.c_int
+    lib.das_merge_attn_states.argtypes = [p, p, p, p, p, p, i64, i32, i32, p]
+    lib.das_merge_attn_states.restype = ctypes.c_int
+    lib.das_strerror.argtypes = [ctypes.c_int]
+    lib.das_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def das_strerror(status: int) -> str:
+    return load_library().das_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != DAS_OK:
+        raise DasError(status, where)
+
+
+def das_plan(B: int, Hkv: int, G: int, Smax: int, D: int, num_splits: int = 0,
+             num_cus: int = 0) -> Tuple[int, int]:
+    """(number of splits, rows per split) the library will use."""
+    ns, chunk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().das_plan(B, Hkv, G, Smax, D, num_splits, num_cus,
+                                   ctypes.byref(ns), ctypes.byref(chunk)), "das_plan")
+    return ns.value, chunk.value
+
+
+def das_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Smax: int, D: int,
+                               num_splits: int = 0, num_cus: int = 0) -> int:
+    n = load_library().das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, num_splits, num_cus)
+    if n == ctypes.c_size_t(-1).value:
+        raise DasError(DAS_EINVAL, "das_decode_workspace_bytes")
+    return int(n)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _decode_shapes(q, k_cache, v_cache, seq_lens):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("q, k_cache and v_cache must be bfloat16")
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,D]; k_cache, v_cache must be [B,Hkv,Smax,D]")
+    B, Hq, D = q.shape
+    _, Hkv, Smax, _ = k_cache.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or seq_lens.shape != (B,):
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    return B, Hq, Hkv, Smax, D
+
+
+def _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse):
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (B, Hq, D) \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 or bfloat16 [B,Hq,D] tensor")
+    if lse_out is None and with_lse:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse_out is not None and (lse_out.dtype != torch.float32 or lse_out.shape != (B, Hq)
+                                or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must be a contiguous float32 [B,Hq] tensor")
+    return out, lse_out
+
+
+def _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace):
+    need = das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, num_splits)
+    if workspace is None:
+        # zero-filled: the workspace starts with the library's arrival counters
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _run_decode(fn_name, q, k_cache, v_cache, seq_lens, scale, out, lse_out, out_dtype,
+                num_splits, workspace, stream, with_lse):
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
+    dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    fn = getattr(load_library(), fn_name)
+    _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, Smax, D,
+              float(scale), _ptr(out), dtype_code, _ptr(lse_out), int(num_splits),
+              _ptr(workspace), ws_bytes, _stream(stream)), fn_name)
+    return out, lse_out, workspace
+
+
+class PreparedCall:
+    """One C-ABI call with its argument list marshalled once.
+
+    For launch loops (benchmarks, serving steps) where the same tensors are
+    used over and over: calling it re-issues the C call with the stored
+    pointers and sizes, skipping the Python-side shape checks.  It keeps the
+    tensors it points to alive."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._fn = getattr(load_library(), name)
+        self._name = name
+        self._args = args
+        self._keep = keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != DAS_OK:
+            raise DasError(rc, self._name)
+
+
+def prepare_decode(fn_name: str, q, k_cache, v_cache, seq_lens, scale: float,
+                   out: torch.Tensor, lse_out: Optional[torch.Tensor], num_splits: int,
+                   workspace: torch.Tensor, stream=None) -> PreparedCall:
+    """Prepared das_decode_attention / das_split_kv_decode call (same checks once)."""
+    if fn_name not in ("das_decode_attention", "das_split_kv_decode"):
+        raise ValueError(fn_name)
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out.dtype, lse_out is not None)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, num_splits):
+        raise DasError(DAS_EWORKSPACE, fn_name)
+    code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, Smax, D,
+            ctypes.c_float(scale), _ptr(out), code, _ptr(lse_out), int(num_splits),
+            _ptr(workspace), ws_bytes, _stream(stream))
+    return PreparedCall(fn_name, args, (q, k_cache, v_cache, seq_lens, out, lse_out, workspace))
+
+
+def prepare_lse_combine(seq_lens, Hq: int, Hkv: int, Smax: int, D: int, workspace, out,
+                        lse_out=None, num_splits: int = 0, stream=None) -> PreparedCall:
+    """Prepared das_lse_combine call."""
+    B = seq_lens.shape[0]
+    code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    args = (_ptr(seq_lens), B, Hq, Hkv, Smax, D, int(num_splits), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), code, _ptr(lse_out),
+            _stream(stream))
+    return PreparedCall("das_lse_combine", args, (seq_lens, workspace, out, lse_out))
+
+
+def das_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                         lse_out: Optional[torch.Tensor] = None,
+                         out_dtype: torch.dtype = torch.float32, num_splits: int = 0,
+                         workspace: Optional[torch.Tensor] = None, stream=None,
+                         with_lse: bool = True):
+    """Decode attention; returns (out [B,Hq,D], lse [B,Hq] or None)."""
+    out, lse_out, _ = _run_decode("das_decode_attention", q, k_cache, v_cache, seq_lens, scale,
+                                  out, lse_out, out_dtype, num_splits, workspace, stream, with_lse)
+    return out, lse_out
+
+
+def das_split_kv_decode(q, k_cache, v_cache, seq_lens, scale, out=None, lse_out=None,
+                        out_dtype=torch.float32, num_splits=0, workspace=None, stream=None,
+                        with_lse=True):
+    """Phase 1 only; returns (out, lse, workspace).  Finish with das_lse_combine."""
+    return _run_decode("das_split_kv_decode", q, k_cache, v_cache, seq_lens, scale, out, lse_out,
+                       out_dtype, num_splits, workspace, stream, with_lse)
+
+
+def das_lse_combine(seq_lens: torch.Tensor, Hq: int, Hkv: int, Smax: int, D: int,
+                    workspace: torch.Tensor, out: torch.Tensor,
+                    lse_out: Optional[torch.Tensor] = None, num_splits: int = 0, stream=None):
+    """Phase 2 only: merge the partials in ``workspace`` into ``out`` / ``lse_out``."""
+    B = seq_lens.shape[0]
+    dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    _check(load_library().das_lse_combine(
+        _ptr(seq_lens), B, Hq, Hkv, Smax, D, int(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), dtype_code, _ptr(lse_out),
+        _stream(stream)), "das_lse_combine")
+    return out, lse_out
+
+
+def das_merge_attn_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor,
+                          lse_b: torch.Tensor, o_out: Optional[torch.Tensor] = None,
+                          lse_out: Optional[torch.Tensor] = None, stream=None):
+    """LSE merge of two attention states; o_* are [..., D], lse_* are [...]."""
+    if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or o_a.shape[:-1] != lse_a.shape:
+        raise ValueError("merge: shape mismatch")
+    if o_a.dtype != o_b.dtype or o_a.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("o_a and o_b must share dtype float32 or bfloat16")
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    for t in (o_a, o_b, lse_a, lse_b):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("merge inputs must be contiguous device tensors")
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    D = o_a.shape[-1]
+    rows = lse_a.numel()
+    code = DAS_BF16 if o_a.dtype == torch.bfloat16 else DAS_F32
+    _check(load_library().das_merge_attn_states(
+        _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out), _ptr(lse_out), rows, D, code,
+        _stream(stream)), "das_merge_attn_states")
+    return o_out, lse_out

@@ -1,0 +1,287 @@
+// das_api.cpp -- C ABI of the split-KV decode attention library: argument
+// checks, the split plan and the kernel launches.  Declarations and the
+// contract of every entry point are in include/das.h.
+//
+// Split plan: FlashDecoding++ post (TechKnowGenie), §2 (the sequence axis is a
+// third grid axis cut into fixed-size chunks) and §6 "chunk size tuning guide"
+// (small chunks inflate the phase-2 traffic, large chunks leave compute units
+// idle; several times more blocks than compute units).
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "das.h"
+#include "das_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cache[kMaxDevices];
+
+// Workgroups per compute unit the automatic plan aims for.  One 8-wave
+// phase-1 workgroup is resident per CU, so one per CU keeps every split in a
+// single wave of workgroups, each long enough to stream efficiently.
+constexpr int64_t kTargetWgsPerCu = 1;
+constexpr int64_t kMaxChunk = 8192;
+// Even when the batch alone fills the chip, a maximal-length sequence is cut
+// into at least this many splits: with variable lengths the last running
+// workgroups then hold at most a third of the longest sequence.
+constexpr int64_t kMinSplitsLongest = 3;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t q) { return ceil_div(a, q) * q; }
+
+// Smallest chunk the automatic plan uses.  Each split writes G*(D+2) floats
+// of partial state per D*4 bytes of K+V row, so the partial traffic is about
+// 2*G/chunk of the K/V bytes (written once, read once); these floors keep it
+// near 3%.
+int64_t min_chunk(int G) { return G >= 8 ? 512 : 256; }
+
+bool supported_dims(int D, int G) {
+  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+int device_cus(int32_t num_cus, int* out) {
+  if (num_cus > 0) {
+    *out = num_cus;
+    return DAS_OK;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DAS_ELAUNCH;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return DAS_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return DAS_ELAUNCH;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return DAS_OK;
+}
+
+int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t num_splits,
+              int32_t num_cus, int32_t* ns_out, int32_t* chunk_out) {
+  if (B < 1 || B > 65535 || Hkv < 1 || Hkv > 65535 || G < 1 || Smax < 1 || D < 1 ||
+      num_splits < 0 || num_cus < 0)
+    return DAS_EINVAL;
+  if (!supported_dims(D, G)) return DAS_ENOTSUP;
+  if (num_splits > DAS_MAX_SPLITS) return DAS_EINVAL;
+  int64_t chunk;
+  if (num_splits > 0) {
+    chunk = round_up(ceil_div(Smax, num_splits), DAS_CHUNK_QUANTUM);
+  } else {
+    int cus = 0;
+    const int rc = device_cus(num_cus, &cus);
+    if (rc != DAS_OK) return rc;
+    const int64_t units = (int64_t)B * Hkv;
+    const int64_t target = kTargetWgsPerCu * cus;
+    int64_t ns_fill = ceil_div(target, units);
+    if (ns_fill < kMinSplitsLongest) ns_fill = kMinSplitsLongest;
+    chunk = round_up(ceil_div(Smax, ns_fill), DAS_CHUNK_QUANTUM);
+    if (chunk < min_chunk(G)) chunk = min_chunk(G);
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    // never more splits than the combine kernel can hold
+    const int64_t floor_chunk = round_up(ceil_div(Smax, DAS_MAX_SPLITS), DAS_CHUNK_QUANTUM);
+    if (chunk < floor_chunk) chunk = floor_chunk;
+  }
+  const int64_t ns = ceil_div(Smax, chunk);
+  if (ns < 1 || ns > DAS_MAX_SPLITS || chunk > INT32_MAX) return DAS_EINVAL;
+  *ns_out = (int32_t)ns;
+  *chunk_out = (int32_t)chunk;
+  return DAS_OK;
+}
+
+// Workspace: arrival counters (fixed area of das::kCounterBytes), then
+// ws_o [B][Hq][ns][D] floats, then (256-byte aligned) ws_ml [B][Hq][ns][2].
+size_t ws_o_offset() { return das::kCounterBytes; }
+size_t ws_ml_offset(int32_t B, int32_t Hq, int32_t ns, int32_t D) {
+  const size_t end = ws_o_offset() + (size_t)B * Hq * ns * D * sizeof(float);
+  return (end + 255) & ~(size_t)255;
+}
+size_t ws_total(int32_t B, int32_t Hq, int32_t ns, int32_t D) {
+  if (ns <= 1) return 0;
+  return ws_ml_offset(B, Hq, ns, D) + (size_t)B * Hq * ns * 2 * sizeof(float);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Checked {
+  int32_t G, ns, chunk;
+};
+
+// Checks shared by every decode entry point.  Nothing is launched on failure.
+int check_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
+                 int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, const void* out,
+                 int32_t out_dtype, int32_t num_splits, const void* workspace,
+                 size_t workspace_bytes, bool need_inputs, Checked* c) {
+  if (seq_lens == nullptr || out == nullptr) return DAS_EINVAL;
+  if (need_inputs && (q == nullptr || k == nullptr || v == nullptr)) return DAS_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || D < 1) return DAS_EINVAL;
+  if (Hq % Hkv != 0) return DAS_EINVAL;
+  if (out_dtype != DAS_F32 && out_dtype != DAS_BF16) return DAS_EINVAL;
+  if (!std::isfinite(scale)) return DAS_EINVAL;
+  const int32_t G = Hq / Hkv;
+  if (!supported_dims(D, G)) return DAS_ENOTSUP;
+  if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
+  if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
+  int32_t ns = 0, chunk = 0;
+  const int rc = plan_impl(B, Hkv, G, Smax, D, num_splits, 0, &ns, &chunk);
+  if (rc != DAS_OK) return rc;
+  if (ns > 1) {
+    if (workspace == nullptr || !aligned16(workspace)) return DAS_EWORKSPACE;
+    if (workspace_bytes < ws_total(B, Hq, ns, D)) return DAS_EWORKSPACE;
+  }
+  c->G = G;
+  c->ns = ns;
+  c->chunk = chunk;
+  return DAS_OK;
+}
+
+int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
+               int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out,
+               int32_t out_dtype, float* lse_out, void* workspace, const Checked& c, bool fused,
+               hipStream_t st) {
+  das::SplitArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.seq_lens = seq_lens;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Smax = Smax;
+  a.chunk = c.chunk;
+  a.ns = c.ns;
+  a.scale_log2e = scale * 1.44269504088896341f;
+  a.direct = c.ns == 1;
+  a.fused = fused && !a.direct;
+  if (!a.direct) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<unsigned int*>(ws);
+    a.ws_o = reinterpret_cast<float*>(ws + ws_o_offset());
+    a.ws_ml = reinterpret_cast<float*>(ws + ws_ml_offset(B, Hq, c.ns, D));
+  }
+  a.out = out;
+  a.lse = lse_out;
+  a.out_bf16 = out_dtype == DAS_BF16;
+  return das::launch_split_kv_decode(D, c.G, B, a, st) == hipSuccess ? DAS_OK : DAS_ELAUNCH;
+}
+
+int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int32_t D,
+               const void* workspace, void* out, int32_t out_dtype, float* lse_out,
+               const Checked& c, hipStream_t st) {
+  if (c.ns <= 1) return DAS_OK;
+  das::CombineArgs a{};
+  a.seq_lens = seq_lens;
+  const char* ws = static_cast<const char*>(workspace);
+  a.ws_o = reinterpret_cast<const float*>(ws + ws_o_offset());
+  a.ws_ml = reinterpret_cast<const float*>(ws + ws_ml_offset(B, Hq, c.ns, D));
+  a.Hq = Hq;
+  a.Smax = Smax;
+  a.chunk = c.chunk;
+  a.ns = c.ns;
+  a.out = out;
+  a.lse = lse_out;
+  a.out_bf16 = out_dtype == DAS_BF16;
+  return das::launch_lse_combine(D, B, a, st) == hipSuccess ? DAS_OK : DAS_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int das_plan(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t num_splits,
+             int32_t num_cus, int32_t* ns_out, int32_t* chunk_out) {
+  if (ns_out == nullptr || chunk_out == nullptr) return DAS_EINVAL;
+  return plan_impl(B, Hkv, G, Smax, D, num_splits, num_cus, ns_out, chunk_out);
+}
+
+size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                                  int32_t num_splits, int32_t num_cus) {
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return (size_t)-1;
+  int32_t ns = 0, chunk = 0;
+  if (plan_impl(B, Hkv, Hq / Hkv, Smax, D, num_splits, num_cus, &ns, &chunk) != DAS_OK)
+    return (size_t)-1;
+  return ws_total(B, Hq, ns, D);
+}
+
+int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                        int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+                        float* lse_out, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Checked c{};
+  const int rc = check_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
+                              out_dtype, num_splits, workspace, workspace_bytes, true, &c);
+  if (rc != DAS_OK) return rc;
+  return run_phase1(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
+                    lse_out, workspace, c, false, static_cast<hipStream_t>(stream));
+}
+
+int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax,
+                    int32_t D, int32_t num_splits, const void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
+                    void* stream) {
+  Checked c{};
+  const int rc = check_decode(nullptr, nullptr, nullptr, seq_lens, B, Hq, Hkv, Smax, D, 1.0f, out,
+                              out_dtype, num_splits, workspace, workspace_bytes, false, &c);
+  if (rc != DAS_OK) return rc;
+  return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c,
+                    static_cast<hipStream_t>(stream));
+}
+
+int das_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+                         float* lse_out, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Checked c{};
+  const int rc = check_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
+                              out_dtype, num_splits, workspace, workspace_bytes, true, &c);
+  if (rc != DAS_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // One launch: the last workgroup of each (b, kv-head) merges the splits.
+  // Shapes with more (b, kv-head) pairs than counter slots run the merge as
+  // a second kernel instead.
+  const bool fused = (int64_t)B * Hkv <= das::kCounterSlots;
+  const int rc1 = run_phase1(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
+                             out_dtype, lse_out, workspace, c, fused, st);
+  if (rc1 != DAS_OK || fused) return rc1;
+  return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c, st);
+}
+
+int das_merge_attn_states(const void* o_a, const float* lse_a, const void* o_b,
+                          const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                          int32_t D, int32_t o_dtype, void* stream) {
+  if (rows < 0) return DAS_EINVAL;
+  if (o_dtype != DAS_F32 && o_dtype != DAS_BF16) return DAS_EINVAL;
+  if (D != 64 && D != 128) return DAS_ENOTSUP;
+  if (rows == 0) return DAS_OK;
+  if (o_a == nullptr || o_b == nullptr || o_out == nullptr || lse_a == nullptr ||
+      lse_b == nullptr || lse_out == nullptr)
+    return DAS_EINVAL;
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out)) return DAS_EINVAL;
+  if (rows > (int64_t)4 * 2147483647LL) return DAS_EINVAL;
+  das::MergeArgs a{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, o_dtype == DAS_BF16};
+  return das::launch_merge_attn_states(D, a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DAS_OK
+             : DAS_ELAUNCH;
+}
+
+const char* das_strerror(int status) {
+  switch (status) {
+    case DAS_OK: return "success";
+    case DAS_EINVAL: return "invalid argument";
+    case DAS_ENOTSUP: return "unsupported shape (head dim or GQA group)";
+    case DAS_EWORKSPACE: return "workspace missing or too small";
+    case DAS_ELAUNCH: return "HIP launch or device query failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// das_internal.h -- argument blocks and launchers shared by the host API
+// (das_api.cpp) and the gfx950 kernels (das_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace das {
+
+// Phase-1 shape knobs (compile-time; the defaults are the tuned ones).
+#ifndef DAS_WAVES
+#define DAS_WAVES 8          // waves per phase-1 workgroup
+#endif
+#ifndef DAS_TILE
+#define DAS_TILE 32          // K/V rows a wave handles per loop iteration (16 or 32)
+#endif
+#ifndef DAS_PREFETCH
+#define DAS_PREFETCH 0       // 1: load the next tile into registers while computing this one
+#endif
+#ifndef DAS_FUSED_FENCE
+#define DAS_FUSED_FENCE 0    // 1: agent-scope release fence before counting (L2 write-back)
+#endif
+#ifndef DAS_MIN_WAVES_PER_EU
+#define DAS_MIN_WAVES_PER_EU 2  // occupancy the register allocator must allow
+#endif
+
+constexpr int kWaves = DAS_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = DAS_TILE;
+static_assert(kTile == 16 || kTile == 32, "tile must be 16 or 32 rows");
+
+// Phase 1 (FlashDecoding++ post, §3 phase 1).  One workgroup per
+// (split, kv-head, batch row); it holds every query head of that kv-head.
+struct SplitArgs {
+  const uint16_t* q;         // bf16 [B][Hq][D]
+  const uint16_t* k;         // bf16 [B][Hkv][Smax][D]
+  const uint16_t* v;         // bf16 [B][Hkv][Smax][D]
+  const int32_t* seq_lens;   // int32 [B]
+  int32_t Hq, Hkv, Smax;
+  int32_t chunk, ns;         // rows per split, number of splits
+  float scale_log2e;         // scale * log2(e): logits are kept in base-2 units
+  float* ws_o;               // [B][Hq][ns][D] unnormalised partial outputs
+  float* ws_ml;              // [B][Hq][ns][2] (split max in base-2 units, exp2 sum)
+  void* out;                 // single-split plans: [B][Hq][D] f32 or bf16
+  float* lse;                // single-split plans: [B][Hq] natural log, may be null
+  int32_t out_bf16;
+  int32_t direct;            // 1: single split, write out/lse instead of partials
+  int32_t fused;             // 1: the last workgroup of each (b, kv-head) merges the splits
+  unsigned int* counters;    // fused: arrival counters [B][Hkv], zero between calls
+};
+
+// Arrival counters live at the start of the workspace, one per (batch row,
+// kv-head), in a fixed area so that their place never depends on the shape.
+constexpr int kCounterSlots = 65536;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+
+// Phase 2 (same post, §3 phase 2).  One workgroup per (query head, batch row).
+struct CombineArgs {
+  const int32_t* seq_lens;
+  const float* ws_o;
+  const float* ws_ml;
+  int32_t Hq, Smax, chunk, ns;
+  void* out;
+  float* lse;                // may be null
+  int32_t out_bf16;
+};
+
+// Two-state LSE merge (SGLang Diffusion "Parallelism Overview", ring merge).
+struct MergeArgs {
+  const void* o_a;
+  const float* lse_a;
+  const void* o_b;
+  const float* lse_b;
+  void* o_out;
+  float* lse_out;
+  int64_t rows;
+  int32_t bf16;
+};
+
+hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, hipStream_t stream);
+hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
+hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t stream);
+
+}  // namespace das

@@ -1,0 +1,872 @@
+// das_kernels.hip -- gfx950 kernels for split-KV decode attention.
+//
+// Sources (cited by page title and section):
+//   [FD++]    "FlashDecoding++: 시퀀스 차원 KV 분할 병렬화와 GPU 언더유틸라이제이션 극복을 통한
+//             LLM 서빙 극대화" (TechKnowGenie): §2 sequence axis as a grid axis, §3
+//             phase 1 (per-chunk max, exponential sum, unnormalised output) and
+//             phase 2 (global max, exp(m_c - M) rescale, sum, divide).
+//   [SGL-PAR] "병렬 처리 개요 (Parallelism Overview)", SGLang Diffusion docs:
+//             "What happens to the shapes" / "Constraints" -- the LSE merge of
+//             partial attention states.
+//
+// Design notes (MI355X / CDNA4):
+//   * Decode attention reads every K/V row once and does about G flops per
+//     byte, so it is bound by HBM bandwidth.  Phase 1 streams K and V with
+//     16-byte loads in which 16 (D=128) or 8 (D=64) consecutive lanes cover
+//     one 256/128-byte row, so each wave-wide load covers whole rows.
+//   * q.K^T for G in {4, 8} is a real (small) matrix product and runs on the
+//     matrix cores: v_mfma_f32_16x16x32_bf16 with the G query heads as rows
+//     and 16 cached rows as columns.  Its B operand wants one row per lane,
+//     which the coalesced load does not give, so each wave stages its K tile
+//     through LDS with an XOR swizzle that keeps both the store and the
+//     column-major read free of bank conflicts.  For G in {1, 2} the product
+//     is a matrix-vector product and runs on the vector ALUs with
+//     v_dot2_f32_bf16 (exact bf16 products, fp32 accumulation).
+//   * p.V runs on the vector ALUs in fp32 straight from the coalesced V
+//     registers; p reaches the lanes that need it through a small per-wave
+//     LDS buffer.
+//   * The online softmax keeps, per wave and head, a running max (base-2
+//     units: logits are scaled by scale*log2(e) in fp32 after the dot) and
+//     rescales the partial sums only when the max grows.
+//   * The four waves of a workgroup merge their states through LDS at the
+//     end; the workgroup then writes its split's (o, m, l) partial, or, for a
+//     single-split plan, the final output.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "das_internal.h"
+
+namespace das {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &u, sizeof(r));
+  return r;
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+  bf16x2_t r;
+  __builtin_memcpy(&r, &u, sizeof(r));
+  return r;
+}
+
+__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+  uint16_t u;
+  __builtin_memcpy(&u, &h, sizeof(u));
+  return u;
+}
+
+__device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (L > smax ? smax : L); }
+
+// DPP row reductions: max or sum over each 16-lane row, result in every lane
+// of the row (quad swaps, then half-row and row mirrors pair the halves).
+template <bool kMax>
+__device__ __forceinline__ float row_reduce16(float x) {
+  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+
+// Raw buffer descriptor over `bytes` bytes at `base`: loads past the end
+// return zeros, so a split's rows past its end need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Byte offset of the 16-byte chunk `c` of row `r` in a wave's K tile.  Rows
+// are 2*D bytes; chunk slots are XOR-swizzled with the row index so that the
+// 16 lanes that store one row, and the 16 lanes that read one chunk column
+// of 16 rows, each hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_tile_offset(int r, int c) {
+  constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  constexpr int kRowsPerBank = 256 / (2 * D);  // rows per 256-byte LDS bank row
+  return r * (2 * D) + ((c ^ ((r / kRowsPerBank) % kChunks)) << 4);
+}
+
+// Stores and loads with the sc1 cache policy: coherent at device scope, so a
+// workgroup on another XCD (another L2) sees them without an L2 write-back or
+// invalidate.
+constexpr int kCoherent = 16;  // sc1
+
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
+  typedef float f4_t __attribute__((ext_vector_type(4)));
+  const f4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(
+      unsigned int __attribute__((ext_vector_type(4))), w), r, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ void coherent_store8(__amdgpu_buffer_rsrc_t r, int off, float x, float y) {
+  typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
+  const u2_t w = {__float_as_uint(x), __float_as_uint(y)};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent);
+  return make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                     __uint_as_float(w[3]));
+}
+
+__device__ __forceinline__ float2 coherent_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
+  const u2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent);
+  return make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+
+// Four consecutive outputs, f32 or bf16 (round to nearest even).
+__device__ __forceinline__ void store_out4(const SplitArgs& a, size_t e, float x, float y, float z,
+                                           float w) {
+  if (a.out_bf16) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + e;
+    const uint32_t lo = f32_to_bf16_rne(x) | ((uint32_t)f32_to_bf16_rne(y) << 16);
+    const uint32_t hi = f32_to_bf16_rne(z) | ((uint32_t)f32_to_bf16_rne(w) << 16);
+    *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + e) = make_float4(x, y, z, w);
+  }
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1: split_kv_decode.  Grid (ns, Hkv, B), kThreads threads.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decode_kernel(SplitArgs a) {
+  constexpr int kLanesPerRow = D / 8;           // lanes covering one K/V row, 16 B each
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  constexpr int kLoads = kTile / kRowsPerLoad;  // 16-byte loads per lane per tile (K or V)
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kKTileBytes = kTile * kRowBytes;
+  constexpr int kPBytes = kTile * G * 4;
+  constexpr int kWaveBytes = kKTileBytes + kPBytes;
+  constexpr int kMergeBytes = (G * D + 2 * G) * 4;
+  constexpr int kSmemBytes =
+      kWaves * (kWaveBytes > kMergeBytes ? kWaveBytes : kMergeBytes);
+  constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
+  static_assert((kThreads > G * D / 4 ? kThreads : G * D / 4) * 16 + kThreads * 4 +
+                        kWaves * G * 4 <= kSmemBytes,
+                "fused merge scratch must fit in the tile LDS");
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = clamp_len(a.seq_lens[b], a.Smax);
+  const int j0 = s * a.chunk;
+  const int j1 = min(j0 + a.chunk, L);
+  // An empty split exits at once; phase 2 never reads it.  With the fused
+  // merge, split 0 of an empty sequence stays to write out = 0, lse = -inf.
+  if (!a.direct && j0 >= L && !(a.fused && s == 0)) return;
+  const int n_rows = j1 > j0 ? j1 - j0 : 0;
+
+  unsigned char* kt = smem + wave * kWaveBytes;
+  float* pt = reinterpret_cast<float*>(kt + kKTileBytes);
+
+  // This split's rows of K and V, as bounds-checked buffers.
+  const size_t slab = (((size_t)b * a.Hkv + g) * (size_t)a.Smax + (size_t)j0) * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + slab, n_rows * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + slab, n_rows * kRowBytes);
+  const int row_in_load = lane / kLanesPerRow;  // this lane's row within a load
+  const int chunk = lane % kLanesPerRow;        // this lane's 16-byte chunk of a row
+  const int lane_off = row_in_load * kRowBytes + 16 * chunk;
+  const float c2 = a.scale_log2e;
+
+  // ---- query operand ----
+  // G >= 4: MFMA A operand; lane i holds head i%16 (zero when >= G) and the
+  //         8 dims of chunk 4*kb + i/16 for k-block kb.
+  // G <= 2: lane i works on row i % kTile and the part i / kTile of D; it
+  //         holds that part of every head as bf16 pairs.
+  constexpr int kParts = 64 / kTile;
+  constexpr int kPartDims = D / kParts;
+  bf16x8_t qa[kKBlocks];
+  uint32_t qv[G <= 2 ? G : 1][G <= 2 ? kPartDims / 2 : 1];
+  if constexpr (G >= 4) {
+    const int hh = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < kKBlocks; ++kb) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (hh < G) {
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + hh) * D;
+        w = *reinterpret_cast<const uint4*>(qrow + 8 * (4 * kb + (lane >> 4)));
+      }
+      qa[kb] = as_bf16x8(w);
+    }
+  } else {
+    const int part = lane / kTile;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)b * a.Hq + (size_t)g * G + h) * D + part * kPartDims);
+#pragma unroll
+      for (int i = 0; i < kPartDims / 8; ++i) {
+        const uint4 w = qrow[i];
+        qv[h][4 * i + 0] = w.x;
+        qv[h][4 * i + 1] = w.y;
+        qv[h][4 * i + 2] = w.z;
+        qv[h][4 * i + 3] = w.w;
+      }
+    }
+  }
+
+  // ---- per-wave running state ----
+  constexpr int kLaneHeads = G >= 4 ? 4 : G;
+  float m_run[G];               // running max per head (base-2 units), wave-uniform
+  float acc[G][8];              // p.V partial sums for this lane's chunk of D
+  float l_lane[kLaneHeads];     // exponential sums of the logits this lane holds
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kLaneHeads; ++i) l_lane[i] = 0.f;
+
+  auto load_tile = [&](int r0, uint4* kr, uint4* vr) {
+    const int soff = r0 * kRowBytes;
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m) {
+      const int voff = lane_off + m * kRowsPerLoad * kRowBytes;
+      kr[m] = buffer_load16(rk, voff, soff);
+      vr[m] = buffer_load16(rv, voff, soff);
+    }
+  };
+
+  auto process_tile = [&](int r0, const uint4* kr, const uint4* vr) {
+    // stage K through LDS (swizzled)
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m)
+      *reinterpret_cast<uint4*>(kt + k_tile_offset<D>(kRowsPerLoad * m + row_in_load, chunk)) = kr[m];
+    wave_lds_fence();
+
+    float alpha[G];
+    bool grow = false;
+    if constexpr (G >= 4) {
+      constexpr int kHeadGroups = G / 4;
+      constexpr int kColGroups = kTile / 16;
+      const int n = lane & 15;
+      float x[kColGroups][4];
+#pragma unroll
+      for (int tg = 0; tg < kColGroups; ++tg) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kKBlocks; ++kb) {
+          const uint4 kw = *reinterpret_cast<const uint4*>(
+              kt + k_tile_offset<D>(16 * tg + n, 4 * kb + (lane >> 4)));
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], as_bf16x8(kw), sacc, 0, 0, 0);
+        }
+        const bool ok = r0 + 16 * tg + n < n_rows;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[tg][r] = ok ? sacc[r] * c2 : -INFINITY;
+      }
+      // tile max per head: row 16*hg .. 16*hg+15 of the wave holds heads 4*hg + r
+      float mt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mt[r] = x[0][r];
+#pragma unroll
+        for (int tg = 1; tg < kColGroups; ++tg) mt[r] = fmaxf(mt[r], x[tg][r]);
+        mt[r] = row_reduce16<true>(mt[r]);
+      }
+#pragma unroll
+      for (int hg = 0; hg < kHeadGroups; ++hg) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * hg + r;
+          const float mn = fmaxf(m_run[h], lane_value(mt[r], 16 * hg));
+          grow |= mn > m_run[h];
+          alpha[h] = fast_exp2(m_run[h] - mn);
+          m_run[h] = mn;
+        }
+      }
+      const bool upper = kHeadGroups == 2 && lane >= 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ml = upper ? m_run[(4 + r) % G] : m_run[r];
+        const float al = upper ? alpha[(4 + r) % G] : alpha[r];
+        float lsum = 0.f;
+#pragma unroll
+        for (int tg = 0; tg < kColGroups; ++tg) {
+          x[tg][r] = fast_exp2(x[tg][r] - ml);
+          lsum += x[tg][r];
+        }
+        l_lane[r] = fmaf(l_lane[r], al, lsum);
+      }
+      if (lane < 16 * kHeadGroups) {
+#pragma unroll
+        for (int tg = 0; tg < kColGroups; ++tg)
+          *reinterpret_cast<float4*>(pt + (16 * tg + n) * G + 4 * (lane >> 4)) =
+              make_float4(x[tg][0], x[tg][1], x[tg][2], x[tg][3]);
+      }
+    } else {
+      // lane i: row i % kTile, part i / kTile of D; then add the parts
+      const int n = lane % kTile, part = lane / kTile;
+      float x[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) x[h] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < kPartDims / 8; ++cc) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(
+            kt + k_tile_offset<D>(n, part * (kPartDims / 8) + cc));
+        const uint32_t kwv[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][4 * cc + i]), as_bf16x2(kwv[i]),
+                                                   x[h], false);
+      }
+      const bool ok = r0 + n < n_rows;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int off = kTile; off < 64; off <<= 1) x[h] += xor_shfl(x[h], off);
+        x[h] = ok ? x[h] * c2 : -INFINITY;
+        const float mt = row_reduce16<true>(x[h]);
+        float tile_max = lane_value(mt, 0);
+        if constexpr (kTile == 32) tile_max = fmaxf(tile_max, lane_value(mt, 16));
+        const float mn = fmaxf(m_run[h], tile_max);
+        grow |= mn > m_run[h];
+        alpha[h] = fast_exp2(m_run[h] - mn);
+        m_run[h] = mn;
+        const float p = fast_exp2(x[h] - mn);
+        l_lane[h] = fmaf(l_lane[h], alpha[h], part == 0 ? p : 0.f);
+        x[h] = p;
+      }
+      if (part == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pt[n * G + h] = x[h];
+      }
+    }
+    wave_lds_fence();
+
+    // ---- p.V on the vector ALUs ----
+    if (grow) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+    }
+#pragma unroll
+    for (int m = 0; m < kLoads; ++m) {
+      const int r = kRowsPerLoad * m + row_in_load;
+      float ph[G];
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int h4 = 0; h4 < G / 4; ++h4) {
+          const float4 w = *reinterpret_cast<const float4*>(pt + r * G + 4 * h4);
+          ph[4 * h4 + 0] = w.x;
+          ph[4 * h4 + 1] = w.y;
+          ph[4 * h4 + 2] = w.z;
+          ph[4 * h4 + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) ph[h] = pt[r * G + h];
+      }
+      const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = bf16_lo(vw[i]);
+        vf[2 * i + 1] = bf16_hi(vw[i]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[h], vf[e], acc[h][e]);
+    }
+  };
+
+  const int stride = kWaves * kTile;
+  if constexpr (DAS_PREFETCH) {
+    int r0 = wave * kTile;
+    if (r0 < n_rows) {
+      uint4 ka[kLoads], va[kLoads], kb_[kLoads], vb[kLoads];
+      load_tile(r0, ka, va);
+      while (true) {
+        const int r1 = r0 + stride;
+        if (r1 < n_rows) load_tile(r1, kb_, vb);
+        process_tile(r0, ka, va);
+        if (r1 >= n_rows) break;
+        const int r2 = r1 + stride;
+        if (r2 < n_rows) load_tile(r2, ka, va);
+        process_tile(r1, kb_, vb);
+        if (r2 >= n_rows) break;
+        r0 = r2;
+      }
+    }
+  } else {
+    for (int r0 = wave * kTile; r0 < n_rows; r0 += stride) {
+      uint4 kr[kLoads], vr[kLoads];
+      load_tile(r0, kr, vr);
+      process_tile(r0, kr, vr);
+    }
+  }
+
+  // ---- wave totals ----
+  // acc: sum the lanes that share a chunk of D (the rows of one load)
+#pragma unroll
+  for (int off = kLanesPerRow; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += xor_shfl(acc[h][e], off);
+  float l_tot[G];
+  if constexpr (G >= 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_lane[r] = row_reduce16<false>(l_lane[r]);
+#pragma unroll
+    for (int hg = 0; hg < G / 4; ++hg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l_tot[4 * hg + r] = lane_value(l_lane[r], 16 * hg);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float t = row_reduce16<false>(l_lane[h]);
+      l_tot[h] = lane_value(t, 0) + (kTile == 32 ? lane_value(t, 16) : 0.f);
+    }
+  }
+
+  // ---- merge the waves through LDS ----
+  __syncthreads();  // every wave is done with its K tile and p buffer
+  float* mg = reinterpret_cast<float*>(smem + wave * kMergeBytes);
+  if (lane < kLanesPerRow) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *reinterpret_cast<float4*>(mg + h * D + 8 * lane) =
+          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(mg + h * D + 8 * lane + 4) =
+          make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mg[G * D + h] = m_run[h];
+      mg[G * D + G + h] = l_tot[h];
+    }
+  }
+  __syncthreads();
+
+  // A sequence that uses at most one split is finished by split 0's
+  // workgroup; so is every sequence of a single-split plan.
+  const int nsb = (L + a.chunk - 1) / a.chunk;
+  const bool finish_here = a.direct || (a.fused && nsb <= 1);
+  constexpr int kQuads = D / 4;                 // float4 quads per output row
+  // Partials of this (b, kv-head): rows (head, split) of D floats, and
+  // (max, sum) pairs.  Offsets stay far below 4 GiB within one kv-head.
+  const size_t qh0 = (size_t)b * a.Hq + (size_t)g * G;   // first query head of the group
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(a.ws_o + (a.direct ? 0 : qh0 * a.ns * D), G * a.ns * D * 4);
+  const __amdgpu_buffer_rsrc_t rml =
+      make_rsrc(a.ws_ml + (a.direct ? 0 : qh0 * a.ns * 2), G * a.ns * 2 * 4);
+  for (int idx = tid; idx < G * kQuads; idx += kThreads) {
+    const int h = idx / kQuads, quad = idx % kQuads;
+    float mw[kWaves], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* mgw = reinterpret_cast<const float*>(smem + w * kMergeBytes);
+      mw[w] = mgw[G * D + h];
+      M = fmaxf(M, mw[w]);
+    }
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* mgw = reinterpret_cast<const float*>(smem + w * kMergeBytes);
+        const float f = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+        const float4 u = *reinterpret_cast<const float4*>(mgw + h * D + 4 * quad);
+        o.x = fmaf(f, u.x, o.x);
+        o.y = fmaf(f, u.y, o.y);
+        o.z = fmaf(f, u.z, o.z);
+        o.w = fmaf(f, u.w, o.w);
+        lsum = fmaf(f, mgw[G * D + G + h], lsum);
+      }
+    }
+    const size_t qh = qh0 + h;
+    if (finish_here) {
+      const float inv = (M == -INFINITY) ? 0.f : 1.f / lsum;
+      store_out4(a, qh * D + 4 * quad, o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      if (quad == 0 && a.lse != nullptr)
+        a.lse[qh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+    } else {
+      // device-coherent stores (sc1): the merging workgroup may run on another XCD
+      const int row = h * a.ns + s;
+      coherent_store16(ro, (row * D + 4 * quad) * 4, o);
+      if (quad == 0) coherent_store8(rml, row * 8, M, lsum);
+    }
+  }
+  if (!a.fused || finish_here) return;
+
+  // ---- fused phase 2: the last workgroup of this (b, kv-head) to arrive
+  // merges every split's partial (FlashDecoding++ post, §3 phase 2) ----
+  __shared__ int s_last;
+  // This workgroup's partial stores must be complete before it is counted.
+#if DAS_FUSED_FENCE
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#else
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+  __syncthreads();
+  if (tid == 0) {
+    unsigned int* cnt = a.counters + (size_t)b * a.Hkv + g;
+    const unsigned int prev = atomicAdd(cnt, 1u);
+    const bool last = prev == (unsigned int)(nsb - 1);
+    if (last) atomicExch(cnt, 0u);  // leave the counter at zero for the next call
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // thread -> (head, float4 quad of D) pair and a subset of the splits
+  constexpr int kPairs = G * kQuads;
+  constexpr int kGroups = kPairs >= kThreads ? 1 : kThreads / kPairs;
+  constexpr int kPerRound = kThreads / kGroups;
+  float4* red4 = reinterpret_cast<float4*>(smem);                        // [kGroups][kPairs]
+  float* redl = reinterpret_cast<float*>(smem + kGroups * kPairs * 16);  // [kGroups][G]
+  float* redm = redl + kGroups * G;                                      // [kWaves][G]
+
+  // global max of every head over its splits: strided pass + block reduction
+  float mloc[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mloc[hh] = -INFINITY;
+  for (int i = tid; i < G * nsb; i += kThreads) {
+    const int hi = i / nsb, c = i - hi * nsb;
+    const float m = coherent_load8(rml, (hi * a.ns + c) * 8).x;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+      if (hh == hi) mloc[hh] = fmaxf(mloc[hh], m);
+  }
+  __syncthreads();  // the wave-merge reads of the LDS are done
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const float v = row_reduce16<true>(mloc[hh]);
+    const float wmax = fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+                             fmaxf(lane_value(v, 32), lane_value(v, 48)));
+    if (lane == 0) redm[wave * G + hh] = wmax;
+  }
+  __syncthreads();
+  float Mh[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    Mh[hh] = redm[hh];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) Mh[hh] = fmaxf(Mh[hh], redm[w * G + hh]);
+  }
+
+  for (int pair0 = 0; pair0 < kPairs; pair0 += kPerRound) {
+    const int pair = pair0 + tid % kPerRound;
+    const int grp = tid / kPerRound;
+    const bool active = pair < kPairs;
+    const int h = active ? pair / kQuads : 0, quad = active ? pair % kQuads : 0;
+    const size_t qh = qh0 + h;
+    float M = Mh[0];
+#pragma unroll
+    for (int hh = 1; hh < G; ++hh)
+      if (hh == h) M = Mh[hh];
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ls = 0.f;
+    if (active) {
+      // issue the loads of up to 8 splits before using any of them
+      constexpr int kBatch = 8;
+      for (int c0 = grp; c0 < nsb; c0 += kBatch * kGroups) {
+        float2 st[kBatch];
+        float4 u[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int c = c0 + k * kGroups;
+          if (c < nsb) {
+            st[k] = coherent_load8(rml, (h * a.ns + c) * 8);
+            u[k] = coherent_load16(ro, ((h * a.ns + c) * D + 4 * quad) * 4);
+          } else {
+            st[k] = make_float2(-INFINITY, 0.f);
+            u[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const float w = fast_exp2(st[k].x - M);  // 0 for the padding slots
+          o.x = fmaf(w, u[k].x, o.x);
+          o.y = fmaf(w, u[k].y, o.y);
+          o.z = fmaf(w, u[k].z, o.z);
+          o.w = fmaf(w, u[k].w, o.w);
+          ls = fmaf(w, st[k].y, ls);
+        }
+      }
+    }
+    __syncthreads();  // the LDS is free again (previous round or the wave merge)
+    if (active) {
+      red4[grp * kPairs + pair] = o;
+      if (quad == 0) redl[grp * G + h] = ls;
+    }
+    __syncthreads();
+    if (active && grp == 0) {
+      float4 t = o;
+      float lt = 0.f;
+      for (int gi = 0; gi < kGroups; ++gi) lt += redl[gi * G + h];
+      for (int gi = 1; gi < kGroups; ++gi) {
+        const float4 u = red4[gi * kPairs + pair];
+        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      }
+      const float inv = 1.f / lt;
+      store_out4(a, qh * D + 4 * quad, t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+      if (quad == 0 && a.lse != nullptr) a.lse[qh] = (M + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2: lse_combine.  Grid (Hq, B), 256 threads.
+// ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+
+// One workgroup per (query head, batch row).  Thread t owns the float4 quad
+// t % (D/4) of the output row and the splits t / (D/4) + k * groups.  Each
+// thread loads the statistics and partial rows of its first kRegSplits
+// splits together, so a plan with up to groups * kRegSplits splits needs a
+// single round trip to memory; larger plans loop.
+constexpr int kRegSplits = 8;
+
+// max or sum over the workgroup; every thread gets the result
+template <bool kMax>
+__device__ __forceinline__ float block_reduce2(float v, float* red) {
+  auto op = [](float u, float w) { return kMax ? fmaxf(u, w) : u + w; };
+  v = row_reduce16<kMax>(v);
+  v = op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = op(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a) {
+  constexpr int kQuads = D / 4;
+  constexpr int kGroups = kCombineThreads / kQuads;
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float4 part[kGroups][kQuads];
+
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int quad = tid % kQuads, grp = tid / kQuads;
+  const int L = clamp_len(a.seq_lens[b], a.Smax);
+  const int nsb = (L + a.chunk - 1) / a.chunk;  // splits this sequence used
+  const size_t qh = (size_t)b * a.Hq + h;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml + qh * a.ns * 2);
+  const float4* po = reinterpret_cast<const float4*>(a.ws_o + qh * a.ns * D) + quad;
+
+  // one round trip: statistics and partial rows of this thread's first splits
+  float2 st[kRegSplits];
+  float4 pr[kRegSplits];
+#pragma unroll
+  for (int u = 0; u < kRegSplits; ++u) {
+    const int c = grp + u * kGroups;
+    if (c < nsb) {
+      st[u] = ml[c];
+      pr[u] = po[(size_t)c * kQuads];
+    } else {
+      st[u] = make_float2(-INFINITY, 0.f);
+      pr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kRegSplits; ++u) mx = fmaxf(mx, st[u].x);
+  for (int c = grp + kRegSplits * kGroups; c < nsb; c += kGroups) mx = fmaxf(mx, ml[c].x);
+  const float M = block_reduce2<true>(mx, red);
+
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = 0.f;
+  if (nsb > 0) {
+#pragma unroll
+    for (int u = 0; u < kRegSplits; ++u) {
+      const float w = fast_exp2(st[u].x - M);  // exp2(-inf) = 0 for unused slots
+      o.x = fmaf(w, pr[u].x, o.x);
+      o.y = fmaf(w, pr[u].y, o.y);
+      o.z = fmaf(w, pr[u].z, o.z);
+      o.w = fmaf(w, pr[u].w, o.w);
+      ls = fmaf(w, st[u].y, ls);
+    }
+    for (int c = grp + kRegSplits * kGroups; c < nsb; c += kGroups) {
+      const float2 sc = ml[c];
+      const float4 u4 = po[(size_t)c * kQuads];
+      const float w = fast_exp2(sc.x - M);
+      o.x = fmaf(w, u4.x, o.x);
+      o.y = fmaf(w, u4.y, o.y);
+      o.z = fmaf(w, u4.z, o.z);
+      o.w = fmaf(w, u4.w, o.w);
+      ls = fmaf(w, sc.y, ls);
+    }
+  }
+  // every quad of a group saw the same splits: count each split's sum once
+  const float lsum = block_reduce2<false>(quad == 0 ? ls : 0.f, red);
+  part[grp][quad] = o;
+  __syncthreads();
+  if (tid < D) {
+    const float* pf = reinterpret_cast<const float*>(&part[0][0]);
+    float t = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) t += pf[gi * D + tid];
+    const float val = (nsb == 0) ? 0.f : t / lsum;
+    if (a.out_bf16)
+      reinterpret_cast<uint16_t*>(a.out)[qh * D + tid] = f32_to_bf16_rne(val);
+    else
+      reinterpret_cast<float*>(a.out)[qh * D + tid] = val;
+    if (tid == 0 && a.lse != nullptr)
+      a.lse[qh] = (nsb == 0) ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge_attn_states: one wave per row, so that every lane has read the row's
+// two LSE values before lane 0 may overwrite one of them in place.
+// ---------------------------------------------------------------------------
+template <int D, bool kBf16>
+__global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
+  // No contraction into FMAs: wa*oa and wb*ob must round the same way so that
+  // swapping the two states gives bitwise the same result.
+#pragma clang fp contract(off)
+  constexpr int kPer = D / 64;  // elements per lane
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const float la = a.lse_a[row], lb = a.lse_b[row];
+  const float mx = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, lse = -INFINITY;
+  if (mx != -INFINITY) {
+    lse = mx + logf(expf(la - mx) + expf(lb - mx));
+    wa = expf(la - lse);
+    wb = expf(lb - lse);
+  }
+  float oa[kPer], ob[kPer];
+  const size_t base = (size_t)row * D + (size_t)lane * kPer;
+  if constexpr (kBf16) {
+    const uint16_t* pa = reinterpret_cast<const uint16_t*>(a.o_a) + base;
+    const uint16_t* pb = reinterpret_cast<const uint16_t*>(a.o_b) + base;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      oa[i] = __uint_as_float((uint32_t)pa[i] << 16);
+      ob[i] = __uint_as_float((uint32_t)pb[i] << 16);
+    }
+  } else {
+    const float* pa = reinterpret_cast<const float*>(a.o_a) + base;
+    const float* pb = reinterpret_cast<const float*>(a.o_b) + base;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      oa[i] = pa[i];
+      ob[i] = pb[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    // products rounded separately so that swapping a and b is bitwise symmetric
+    const float ta = wa * oa[i];
+    const float tb = wb * ob[i];
+    const float v = (mx == -INFINITY) ? 0.f : ta + tb;
+    if constexpr (kBf16)
+      reinterpret_cast<uint16_t*>(a.o_out)[base + i] = f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(a.o_out)[base + i] = v;
+  }
+  if (lane == 0) a.lse_out[row] = lse;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int D, int G>
+static hipError_t launch_split(int B, const SplitArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)a.ns, (unsigned)a.Hkv, (unsigned)B);
+  hipLaunchKernelGGL((split_kv_decode_kernel<D, G>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, hipStream_t st) {
+  if (D == 128) {
+    switch (G) {
+      case 1: return launch_split<128, 1>(B, a, st);
+      case 2: return launch_split<128, 2>(B, a, st);
+      case 4: return launch_split<128, 4>(B, a, st);
+      case 8: return launch_split<128, 8>(B, a, st);
+    }
+  } else if (D == 64) {
+    switch (G) {
+      case 1: return launch_split<64, 1>(B, a, st);
+      case 2: return launch_split<64, 2>(B, a, st);
+      case 4: return launch_split<64, 4>(B, a, st);
+      case 8: return launch_split<64, 8>(B, a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)a.Hq, (unsigned)B);
+  if (D == 128)
+    hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineThreads), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineThreads), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  dim3 grid((unsigned)((a.rows + 3) / 4));
+  if (D == 128 && a.bf16)
+    hipLaunchKernelGGL((merge_attn_states_kernel<128, true>), grid, dim3(256), 0, st, a);
+  else if (D == 128)
+    hipLaunchKernelGGL((merge_attn_states_kernel<128, false>), grid, dim3(256), 0, st, a);
+  else if (D == 64 && a.bf16)
+    hipLaunchKernelGGL((merge_attn_states_kernel<64, true>), grid, dim3(256), 0, st, a);
+  else if (D == 64)
+    hipLaunchKernelGGL((merge_attn_states_kernel<64, false>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace das

@@ -1,0 +1,191 @@
+/*
+ * das.h -- split-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Single-query (decode-step) softmax attention over a long KV cache, cut
+ * along the sequence into splits that run as separate workgroups, followed by
+ * a log-sum-exp merge of the per-split partial results.
+ *
+ * Sources, cited by page title and section:
+ *   [FD++]    "FlashDecoding++: 시퀀스 차원 KV 분할 병렬화와 GPU 언더유틸라이제이션 극복을
+ *             통한 LLM 서빙 극대화" (TechKnowGenie).  §1: a decode step is one query
+ *             token against the N cached K/V rows, a memory-bound vector-matrix
+ *             product.  §2: the sequence axis becomes a third grid axis, cut
+ *             into chunks.  §3: phase 1 writes, per chunk, the unnormalised
+ *             partial output, the chunk max and the chunk exponential sum;
+ *             phase 2 rescales every chunk by exp(chunk max - global max),
+ *             sums, and divides.  §6 ("chunk size tuning guide"): too small a
+ *             chunk inflates phase-2 traffic, too large a chunk leaves
+ *             compute units idle; aim for several times more blocks than
+ *             compute units.
+ *   [SGL-PAR] "병렬 처리 개요 (Parallelism Overview)", SGLang Diffusion docs.
+ *             "What happens to the shapes" and "Constraints": partial
+ *             attention results over disjoint row sets (ring hops, tail or
+ *             replicated parts) are joined by an online-softmax merge that
+ *             needs each part's softmax log-sum-exp, so an attention kernel
+ *             must export its LSE.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous arrays,
+ *     16-byte aligned.  bf16 means bfloat16 bit patterns (uint16_t storage).
+ *   - The caller owns all memory.  The library never allocates, frees,
+ *     synchronises the device or copies device memory to the host, so every
+ *     call can be recorded into a HIP graph.  It caches only the compute-unit
+ *     count of each device it has seen.
+ *   - Arguments are checked on the host before anything is launched.  On a
+ *     failed check the call returns a negative status, launches nothing and
+ *     leaves every output untouched.  A launch error returns DAS_ELAUNCH.
+ *     No C++ exception crosses this interface.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     stream-ordered; the call returns without waiting for the GPU.
+ *   - Calls are re-entrant.  Concurrent calls must not share a workspace.
+ *   - Supported shapes: head dim D in {64, 128}; GQA group G = Hq / Hkv in
+ *     {1, 2, 4, 8} (Hq a multiple of Hkv); 1 <= B <= 65535; 1 <= Hkv <= 65535;
+ *     1 <= Smax; num_splits <= DAS_MAX_SPLITS.
+ *   - Query head h reads kv-head h / G.
+ *   - Device-side precondition (not checked on the host, since reading
+ *     seq_lens would need a device-to-host copy): 0 <= seq_lens[b] <= Smax.
+ *     Values outside are clamped to [0, Smax].  A sequence of length 0 yields
+ *     out = 0 and lse = -inf (the identity of the merge).
+ *   - LSE is the natural logarithm of sum_j exp(scale * q.k_j).
+ */
+#ifndef DAS_H
+#define DAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DAS_OK = 0,
+  DAS_EINVAL = -1,     /* bad argument: null pointer, bad shape, bad dtype */
+  DAS_ENOTSUP = -2,    /* valid but unsupported: D, G outside the supported set */
+  DAS_EWORKSPACE = -3, /* workspace missing or smaller than das_decode_workspace_bytes */
+  DAS_ELAUNCH = -4,    /* the HIP runtime refused a launch or a device query */
+} das_status;
+
+typedef enum { DAS_F32 = 0, DAS_BF16 = 1 } das_dtype;
+
+#define DAS_MAX_SPLITS 4096
+/* A workspace begins with this many bytes of arrival counters (see
+ * das_decode_attention): zero them before the workspace is first used. */
+#define DAS_WORKSPACE_COUNTER_BYTES (65536 * 4)
+/* Chunks are whole multiples of this many rows (the per-workgroup quantum). */
+#define DAS_CHUNK_QUANTUM 128
+
+/*
+ * Split plan ([FD++] §2 grid, §6 tuning guide).  Pure host function.
+ *   num_splits == 0: automatic.  The plan picks the number of splits NS so
+ *     that B*Hkv*NS workgroups give every compute unit several workgroups,
+ *     with chunk = ceil(Smax/NS) rounded up to DAS_CHUNK_QUANTUM and kept
+ *     between a lower bound (partial-result traffic stays a few percent of
+ *     the K/V bytes) and an upper bound.
+ *   num_splits == n >= 1: chunk = ceil(Smax/n) rounded up to the quantum;
+ *     NS = ceil(Smax/chunk) <= n.
+ *   Sequence b uses ceil(seq_lens[b]/chunk) of the NS splits; the rest exit
+ *     at once.
+ *   num_cus: compute units to plan for; 0 = query the current device (this
+ *     is the only device query, cached per device).
+ * Outputs *ns_out and *chunk_out.  Returns DAS_OK or a negative status.
+ */
+int das_plan(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t num_splits,
+             int32_t num_cus, int32_t* ns_out, int32_t* chunk_out);
+
+/*
+ * Workspace bytes das_decode_attention needs for this shape and split
+ * request (0 when the plan has a single split).  Layout: first
+ * DAS_WORKSPACE_COUNTER_BYTES of arrival counters (one per (b, kv-head)),
+ * then the phase-1 partial results of [FD++] §3: per (b, query head, split)
+ * an unnormalised output row of D floats, then its max and exponential sum.
+ * num_cus as in das_plan.  Returns (size_t)-1 on invalid arguments.
+ */
+size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                                  int32_t num_splits, int32_t num_cus);
+
+/*
+ * Decode attention ([FD++] §1-§3; LSE export per [SGL-PAR] "Constraints").
+ *   q        bf16 [B][Hq][D]
+ *   k_cache  bf16 [B][Hkv][Smax][D]    rows >= seq_lens[b] are never read
+ *   v_cache  bf16 [B][Hkv][Smax][D]
+ *   seq_lens int32 [B]                 valid rows per sequence (device memory)
+ *   scale    multiplies each dot product q.k (typically 1/sqrt(D))
+ *   out      [B][Hq][D], out_dtype DAS_F32 (float) or DAS_BF16 (rounded to
+ *            nearest even)
+ *   lse_out  float [B][Hq] natural-log LSE, or NULL to skip
+ *   num_splits 0 = automatic plan, n >= 1 forces at most n splits (see das_plan)
+ *   workspace, workspace_bytes: device scratch of at least
+ *            das_decode_workspace_bytes(...) bytes (may be NULL when that is 0)
+ *   stream   hipStream_t or NULL
+ * One kernel launch: one workgroup per (split, kv-head, batch row) holding
+ * the whole GQA group of that kv-head computes its split's partial result
+ * (phase 1); the last workgroup of each (b, kv-head) to finish, found with a
+ * device-scope arrival counter in the workspace, merges every split of that
+ * kv-head (phase 2).  A sequence that uses one split, and every sequence of
+ * a single-split plan, is written directly by its workgroup.  (Shapes with
+ * more than 65536 (b, kv-head) pairs run phase 2 as a second kernel.)
+ * Workspace precondition: its first DAS_WORKSPACE_COUNTER_BYTES must be zero
+ * before the workspace is first used (allocate it zero-filled); every
+ * completed call leaves them zero again, whatever the shape.
+ */
+int das_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                         int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+                         float* lse_out, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Phase 1 alone ([FD++] §3, phase 1): the same arguments and checks as
+ * das_decode_attention.  When the plan has more than one split it writes
+ * only the partial results into `workspace` and leaves out/lse_out
+ * untouched; das_lse_combine with the same shape, num_splits and workspace
+ * then finishes the call.  With a single split it writes out/lse_out
+ * directly.  It never touches the workspace's arrival counters.
+ * das_split_kv_decode + das_lse_combine computes what das_decode_attention
+ * computes, with phase 2 as a separate kernel (sums may round differently).
+ */
+int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                        int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+                        float* lse_out, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Phase 2 alone ([FD++] §3, phase 2): merges the partial results that
+ * das_split_kv_decode left in `workspace` (same B, Hq, Hkv, Smax, D,
+ * num_splits, seq_lens) into out / lse_out.  Per (b, h): M = max of the
+ * split maxima, w_c = exp(m_c - M), out = sum w_c o_c / sum w_c l_c,
+ * lse = M + ln(sum w_c l_c).  A no-op returning DAS_OK when the plan has a
+ * single split.
+ */
+int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax,
+                    int32_t D, int32_t num_splits, const void* workspace,
+                    size_t workspace_bytes, void* out, int32_t out_dtype, float* lse_out,
+                    void* stream);
+
+/*
+ * Merge of two attention states over disjoint row sets ([SGL-PAR] "What
+ * happens to the shapes": ring hops merged by online softmax; "Constraints":
+ * tail-pad / replicated parts joined by the same merge).  Per row r:
+ *   mx = max(lse_a, lse_b); both -inf -> (0, -inf);
+ *   lse = mx + ln(exp(lse_a - mx) + exp(lse_b - mx));
+ *   o = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b.
+ *   o_a, o_b, o_out  [rows][D] in o_dtype (DAS_F32 or DAS_BF16)
+ *   lse_a, lse_b, lse_out float [rows]
+ * o_out / lse_out may alias the corresponding a or b arrays.  D in {64, 128};
+ * rows >= 0 (0 is a no-op).  The formula is symmetric: swapping a and b gives
+ * bitwise the same result.
+ */
+int das_merge_attn_states(const void* o_a, const float* lse_a, const void* o_b,
+                          const float* lse_b, void* o_out, float* lse_out, int64_t rows,
+                          int32_t D, int32_t o_dtype, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* das_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAS_H */

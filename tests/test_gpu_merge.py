@@ -1,0 +1,141 @@
+"""das_merge_attn_states and the two-phase entry points against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_split_amd as das
+import oracle
+import workloads
+from gpu_helpers import check_f32, dev, note, run, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _states(rows, D, seed):
+    rng = np.random.default_rng(seed)
+    o = [rng.standard_normal((rows, D)).astype(np.float32) for _ in range(2)]
+    s = [(rng.standard_normal(rows) * 10).astype(np.float32) for _ in range(2)]
+    s[0][::7] = -np.inf
+    s[1][::11] = -np.inf
+    return o, s
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_merge_matches_oracle_and_is_symmetric(D):
+    o, s = _states(1000, D, D)
+    ta = [torch.from_numpy(v).to(dev()) for v in o]
+    ts = [torch.from_numpy(v).to(dev()) for v in s]
+    mo, ml = das.das_merge_attn_states(ta[0], ts[0], ta[1], ts[1])
+    ro, rl = oracle.merge(o[0].astype(np.float64), s[0].astype(np.float64),
+                          o[1].astype(np.float64), s[1].astype(np.float64))
+    torch.cuda.synchronize()
+    check_f32(mo, ml, ro, rl, f"merge D={D}")
+    so, sl = das.das_merge_attn_states(ta[1], ts[1], ta[0], ts[0])
+    torch.cuda.synchronize()
+    assert torch.equal(mo, so) and torch.equal(ml, sl), "merge must be bitwise symmetric"
+    ident_o, ident_l = das.das_merge_attn_states(ta[0], ts[0], torch.zeros_like(ta[0]),
+                                                 torch.full_like(ts[0], -math.inf))
+    torch.cuda.synchronize()
+    fin = torch.isfinite(ts[0])
+    assert torch.allclose(ident_o[fin], ta[0][fin], atol=1e-6)
+    assert torch.allclose(ident_l[fin], ts[0][fin], atol=1e-6)
+
+
+def test_merge_in_place_and_bf16():
+    o, s = _states(333, 128, 5)
+    ta = [torch.from_numpy(v).to(dev()) for v in o]
+    ts = [torch.from_numpy(v).to(dev()) for v in s]
+    want_o, want_l = das.das_merge_attn_states(ta[0], ts[0], ta[1], ts[1])
+    a_o, a_l = ta[0].clone(), ts[0].clone()
+    das.das_merge_attn_states(a_o, a_l, ta[1], ts[1], o_out=a_o, lse_out=a_l)
+    torch.cuda.synchronize()
+    assert torch.equal(a_o, want_o) and torch.equal(a_l, want_l)
+    bo, bl = das.das_merge_attn_states(ta[0].bfloat16(), ts[0], ta[1].bfloat16(), ts[1])
+    ro, rl = oracle.merge(ta[0].bfloat16().double().cpu().numpy(), s[0].astype(np.float64),
+                          ta[1].bfloat16().double().cpu().numpy(), s[1].astype(np.float64))
+    torch.cuda.synchronize()
+    assert float(torch.max(torch.abs(bo.double().cpu() - torch.from_numpy(ro)))) <= 2 ** -7 * 8
+    assert float(np.max(np.abs(bl.cpu().numpy()[np.isfinite(rl)] - rl[np.isfinite(rl)]))) <= 1e-5
+
+
+def test_merging_two_half_sequences_equals_whole():
+    """Decode over rows [0, m) and [m, L) separately, merge on the GPU: equals decode over [0, L)."""
+    cfg = workloads.custom_config(2, 16, 4, 128, 3000, k_mult=4.0)
+    x = workloads.make_inputs(cfg, 77, seq_lens=(3000, 2100))
+    m = 1300
+    q, k, v, sl = upload(x)
+    whole_o, whole_l = run(x, 0, tensors=(q, k, v, sl))
+    first = das.das_decode_attention(q, k, v, torch.clamp(sl, max=m), x.scale)
+    second = das.das_decode_attention(q, k[:, :, m:].contiguous(), v[:, :, m:].contiguous(),
+                                      torch.clamp(sl - m, min=0), x.scale)
+    mo, ml = das.das_merge_attn_states(first[0], first[1], second[0], second[1])
+    torch.cuda.synchronize()
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    check_f32(mo, ml, *ref, "merged halves")
+    assert float(torch.max(torch.abs(mo - whole_o))) <= 5e-4
+
+
+def test_two_phase_entry_points_match_the_fused_call():
+    """das_split_kv_decode + das_lse_combine (two kernels) computes what the fused
+    das_decode_attention computes; only the merge's summation order differs."""
+    cfg = workloads.CONFIGS[1]
+    x = workloads.make_inputs(cfg, 5, smax=4096, seq_lens=(4000,))
+    q, k, v, sl = upload(x)
+    o1, l1 = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=0)
+    out, lse, ws = das.das_split_kv_decode(q, k, v, sl, x.scale, num_splits=0)
+    das.das_lse_combine(sl, cfg.Hq, cfg.Hkv, 4096, cfg.D, ws, out, lse, num_splits=0)
+    torch.cuda.synchronize()
+    assert float(torch.max(torch.abs(o1 - out))) <= 1e-5
+    assert float(torch.max(torch.abs(l1 - lse))) <= 1e-5
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    check_f32(out, lse, *ref, "two-phase entry points")
+
+
+def test_fused_merge_leaves_counters_zero_and_repeats_exactly():
+    """The arrival counters at the start of the workspace are back at zero after
+    every call, so back-to-back calls on one workspace give bitwise the same result."""
+    cfg = workloads.custom_config(3, 32, 8, 128, 6000)
+    x = workloads.make_inputs(cfg, 6, seq_lens=(6000, 2500, 129))
+    q, k, v, sl = upload(x)
+    need = das.das_decode_workspace_bytes(3, 32, 8, 6000, 128, 7)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    first = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=7, workspace=ws)
+    torch.cuda.synchronize()
+    counters = ws[:das.DAS_WORKSPACE_COUNTER_BYTES].view(torch.int32)
+    assert int(torch.count_nonzero(counters)) == 0
+    for _ in range(3):
+        again = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=7, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1])
+    assert int(torch.count_nonzero(counters)) == 0
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    check_f32(*first, *ref, "fused merge, forced 7 splits")
+
+
+def test_graph_capture_replays_match_eager():
+    cfg = workloads.custom_config(4, 32, 8, 128, 4096)
+    x = workloads.make_inputs(cfg, 9, seq_lens=(4096, 1000, 1, 3000))
+    q, k, v, sl = upload(x)
+    eager_o, eager_l = das.das_decode_attention(q, k, v, sl, x.scale)
+    out = torch.empty_like(eager_o)
+    lse = torch.empty_like(eager_l)
+    ws = torch.zeros(max(das.das_decode_workspace_bytes(4, 32, 8, 4096, 128), 16),
+                     dtype=torch.uint8, device=dev())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        das.das_decode_attention(q, k, v, sl, x.scale, out=out, lse_out=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        das.das_decode_attention(q, k, v, sl, x.scale, out=out, lse_out=lse, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), f"replay {i}"
+        _ = (torch.ones(1000, device=dev()) * 2).sum().item()   # eager work between replays
+    note("graph replays match eager")

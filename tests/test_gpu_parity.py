@@ -1,0 +1,95 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Tolerances: fp32 output max|err| <= 5e-4, LSE max|err| <= 1e-4; bf16 output
+within 1 bf16 ulp of the oracle rounded to bf16 where |oracle| >= 2^-12 and
+within 2^-19 absolute below that.  Rows past seq_lens are NaN in every cache."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_split_amd as das
+import oracle
+import workloads
+from gpu_helpers import check_bf16, check_f32, note, run, upload
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("D,G", SHAPES, ids=lambda v: str(v))
+def test_small_shapes_all_split_counts(D, G):
+    """Several tiles, a ragged tail, two sequences, every supported (D, G)."""
+    cfg = workloads.custom_config(2, 2 * G, 2, D, 1000, k_mult=2.0)
+    x = workloads.make_inputs(cfg, 1000 + 10 * D + G, seq_lens=(1000, 777))
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    for ns in (0, 1, 2, 3, 7, 8):
+        note(f"case D={D} G={G} num_splits={ns}")
+        out, lse = run(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"D={D} G={G} ns={ns}")
+
+
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2)], ids=lambda v: str(v))
+def test_edge_lengths(D, G):
+    """Lengths around the 16/32-row tiles and the 128-row chunk quantum, with
+    empty splits (forced split counts larger than a sequence needs) and L=0."""
+    lens = (0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300)
+    cfg = workloads.custom_config(len(lens), 2 * G, 2, D, 300)
+    x = workloads.make_inputs(cfg, 2000 + D + G, seq_lens=lens)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    for ns in (0, 1, 2, 3):
+        note(f"case edge lengths D={D} G={G} num_splits={ns}")
+        out, lse = run(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"edge D={D} G={G} ns={ns}")
+        assert torch.all(out[0] == 0) and torch.all(lse[0] == -float("inf"))
+
+
+@pytest.mark.parametrize("D,G", [(128, 4), (64, 1), (128, 8)], ids=lambda v: str(v))
+def test_bf16_output(D, G):
+    cfg = workloads.custom_config(3, 4 * G, 4, D, 2000, k_mult=4.0)
+    x = workloads.make_inputs(cfg, 3000 + D + G, seq_lens=(2000, 1, 1234))
+    ref_o, ref_l = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    for ns in (0, 1):
+        note(f"case bf16 D={D} G={G} num_splits={ns}")
+        out, lse = run(x, ns, out_dtype=torch.bfloat16, tensors=t)
+        assert out.dtype == torch.bfloat16
+        check_bf16(out, ref_o, f"bf16 D={D} G={G} ns={ns}")
+        lse_err = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
+        assert lse_err <= 1e-4
+
+
+def test_deterministic_run_to_run():
+    x = workloads.make_inputs(workloads.custom_config(2, 32, 8, 128, 5000), 4000, seq_lens=(5000, 4097))
+    t = upload(x)
+    a = run(x, 0, tensors=t)
+    b = run(x, 0, tensors=t)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("idx", range(5), ids=[c.name for c in workloads.CONFIGS])
+def test_named_config_full_size(idx):
+    """Every named config at its full size, in the automatic launch configuration
+    the benchmark times, against the oracle over all outputs; then the same
+    inputs with num_splits=1 (split invariance)."""
+    cfg = workloads.CONFIGS[idx]
+    note(f"case full config {cfg.name}: generating inputs")
+    x = workloads.config_inputs(idx)
+    ns, chunk = das.das_plan(len(x.seq_lens), cfg.Hkv, cfg.G, x.k.shape[2], cfg.D)
+    note(f"case full config {cfg.name}: plan ns={ns} chunk={chunk}; oracle")
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    note(f"case full config {cfg.name}: auto splits")
+    out, lse = run(x, 0, tensors=t)
+    check_f32(out, lse, *ref, f"{cfg.name} auto")
+    note(f"case full config {cfg.name}: num_splits=1")
+    out1, lse1 = run(x, 1, tensors=t)
+    check_f32(out1, lse1, *ref, f"{cfg.name} ns=1")
+    d_o = float(torch.max(torch.abs(out1 - out)))
+    d_l = float(torch.max(torch.abs(lse1 - lse)))
+    note(f"  split invariance: max|out diff| {d_o:.2e}, max|lse diff| {d_l:.2e}")
+    assert d_o <= 5e-4 and d_l <= 1e-4
+    del t
+    torch.cuda.empty_cache()

@@ -1,0 +1,142 @@
+"""Host-side logic of the C ABI, on the CPU: exported symbols, argument
+checks (nothing is launched when a check fails) and the split plan."""
+import ctypes
+import math
+import os
+import subprocess
+
+import pytest
+
+import decode_attention_split_amd as das
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "das.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(das.LIB_PATH):
+        from decode_attention_split_amd import build
+        build.build()
+    return das.load_library()
+
+
+def _header_functions():
+    import re
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(das_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    declared = _header_functions()
+    assert set(declared) == set(das.EXPORTED)
+    nm = subprocess.run(["nm", "-D", "--defined-only", das.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, f"{name} declared in das.h but not exported"
+        getattr(lib, name)
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert das.das_strerror(code)
+    assert "unknown" in das.das_strerror(7)
+
+
+def plan(B, Hkv, G, Smax, D, ns=0, cus=256):
+    return das.das_plan(B, Hkv, G, Smax, D, ns, cus)
+
+
+@pytest.mark.parametrize("B,Hkv,G,Smax,D", [
+    (1, 8, 8, 1024, 64), (1, 8, 4, 32768, 128), (1, 8, 4, 131072, 128),
+    (64, 8, 4, 16384, 128), (8, 8, 8, 100003, 128), (3, 2, 1, 1, 64), (1, 1, 2, 5000000, 128)])
+def test_auto_plan_covers_the_sequence(B, Hkv, G, Smax, D):
+    ns, chunk = plan(B, Hkv, G, Smax, D)
+    assert chunk % das.DAS_CHUNK_QUANTUM == 0
+    assert 1 <= ns <= das.DAS_MAX_SPLITS
+    assert (ns - 1) * chunk < Smax <= ns * chunk       # every row in exactly one split
+    if ns > 1:                                          # partial traffic floor
+        assert chunk >= (512 if G == 8 else 256)
+
+
+def test_auto_plan_fills_the_chip_for_long_single_sequences():
+    ns, chunk = plan(1, 8, 4, 32768, 128)
+    assert 8 * ns >= 256                                # at least one workgroup per compute unit
+    ns2, _ = plan(1, 8, 4, 131072, 128)
+    assert 8 * ns2 >= 256
+
+
+def test_forced_splits():
+    for n in (1, 2, 3, 7, 64, 300):
+        ns, chunk = plan(1, 8, 4, 32768, 128, ns=n)
+        assert ns <= n and chunk % das.DAS_CHUNK_QUANTUM == 0
+        assert (ns - 1) * chunk < 32768 <= ns * chunk
+        assert chunk == math.ceil(math.ceil(32768 / n) / 128) * 128
+    assert plan(1, 8, 4, 32768, 128, ns=1) == (1, 32768)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 8, 3, 1024, 128), das.DAS_ENOTSUP),      # G = 3
+    ((1, 8, 4, 1024, 96), das.DAS_ENOTSUP),       # D = 96
+    ((0, 8, 4, 1024, 128), das.DAS_EINVAL),
+    ((1, 0, 4, 1024, 128), das.DAS_EINVAL),
+    ((1, 8, 4, 0, 128), das.DAS_EINVAL),
+    ((70000, 8, 4, 1024, 128), das.DAS_EINVAL),
+])
+def test_plan_rejects(args, status):
+    with pytest.raises(das.DasError) as e:
+        das.das_plan(*args, 0, 256)
+    assert e.value.status == status
+
+
+def test_plan_rejects_too_many_splits():
+    with pytest.raises(das.DasError):
+        das.das_plan(1, 8, 4, 1 << 20, 128, das.DAS_MAX_SPLITS + 1, 256)
+
+
+def test_workspace_bytes(lib):
+    B, Hq, Hkv, Smax, D = 64, 32, 8, 16384, 128
+    ns, chunk = plan(B, Hkv, Hq // Hkv, Smax, D)
+    n = das.das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, 0, 256)
+    o_end = das.DAS_WORKSPACE_COUNTER_BYTES + B * Hq * ns * D * 4
+    assert n == ((o_end + 255) // 256) * 256 + B * Hq * ns * 2 * 4
+    assert das.das_decode_workspace_bytes(1, 8, 8, 1024, 64, 1, 256) == 0   # one split: none
+    with pytest.raises(das.DasError):
+        das.das_decode_workspace_bytes(1, 6, 4, 1024, 64, 0, 256)           # Hq % Hkv
+
+
+def _call_decode(lib, **kw):
+    a = dict(q=16, k=16, v=16, sl=16, B=1, Hq=8, Hkv=2, Smax=1024, D=128, scale=0.1, out=16,
+             dt=0, lse=0, ns=4, ws=16, wsb=1 << 30, st=None)
+    a.update(kw)
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.das_decode_attention(P(a["q"]), P(a["k"]), P(a["v"]), P(a["sl"]), a["B"], a["Hq"],
+                                    a["Hkv"], a["Smax"], a["D"], a["scale"], P(a["out"]), a["dt"],
+                                    P(a["lse"]), a["ns"], P(a["ws"]), a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), das.DAS_EINVAL), (dict(k=0), das.DAS_EINVAL), (dict(v=0), das.DAS_EINVAL),
+    (dict(sl=0), das.DAS_EINVAL), (dict(out=0), das.DAS_EINVAL),
+    (dict(Hq=6, Hkv=4), das.DAS_EINVAL), (dict(Hq=6, Hkv=2), das.DAS_ENOTSUP),
+    (dict(D=80), das.DAS_ENOTSUP), (dict(dt=5), das.DAS_EINVAL), (dict(B=0), das.DAS_EINVAL),
+    (dict(Smax=0), das.DAS_EINVAL), (dict(ns=-1), das.DAS_EINVAL),
+    (dict(scale=float("nan")), das.DAS_EINVAL), (dict(q=24), das.DAS_EINVAL),
+    (dict(ws=0), das.DAS_EWORKSPACE), (dict(wsb=100), das.DAS_EWORKSPACE),
+    (dict(ns=das.DAS_MAX_SPLITS + 1), das.DAS_EINVAL),
+])
+def test_decode_argument_checks(lib, kw, status):
+    # All pointers are fake: a failed check must return before any launch.
+    assert _call_decode(lib, **kw) == status
+
+
+def test_merge_argument_checks(lib):
+    P = ctypes.c_void_p
+    f = lib.das_merge_attn_states
+    assert f(P(16), P(16), P(16), P(16), P(16), P(16), -1, 128, 0, None) == das.DAS_EINVAL
+    assert f(P(16), P(16), P(16), P(16), P(16), P(16), 4, 96, 0, None) == das.DAS_ENOTSUP
+    assert f(P(16), P(16), P(16), P(16), P(16), P(16), 4, 128, 9, None) == das.DAS_EINVAL
+    assert f(None, P(16), P(16), P(16), P(16), P(16), 4, 128, 0, None) == das.DAS_EINVAL
+    assert f(P(8), P(16), P(16), P(16), P(16), P(16), 4, 128, 0, None) == das.DAS_EINVAL
+    assert f(None, None, None, None, None, None, 0, 128, 0, None) == das.DAS_OK  # empty
