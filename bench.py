@@ -1,0 +1,252 @@
+"""Benchmark: KV-cache read GB/s (and µs per call) of split-KV decode attention.
+
+One step = one decode-attention call (das_decode_attention: phase 1 with
+the phase-2 merge fused into the last workgroup of each (batch row,
+kv-head), a single kernel launch) over the synthetic workload, with every
+input already resident in HBM.  K/V are rotated over several copies so that repeated steps read
+from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line on stdout.  Also reports, for the dominant (and only)
+kernel, the achieved algorithmic HBM bandwidth against the MI355X peak,
+measured with HIP events on the launch stream around the timed launches,
+and the fp64 CPU oracle's throughput on a bounded sample of the same
+workload (the reported CPU baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-cache read GB/s (% of HBM peak) and µs per decode-attention call"
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+LLC_BYTES = 256 << 20     # MI355X Infinity Cache
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="index into workloads.CONFIGS")
+    ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
+    ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate; 0 = auto")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time for the oracle baseline; 0 skips it")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy() -> None:
+    """A plain 256 MiB device-to-device copy, 10 times: the reference whose
+    FETCH_SIZE / WRITE_SIZE counters scale the decode kernel's counters."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "launches": 10}), flush=True)
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in ("decode_attention_split_amd/csrc/das_kernels.hip",
+                "decode_attention_split_amd/csrc/das_internal.h",
+                "decode_attention_split_amd/csrc/das_api.cpp"):
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, ns: int):
+    """HBM bytes per launch from the committed counter summary, when it was
+    taken on the current kernel source and this workload; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"split_kv_decode_{workload}_counters.json")
+    try:
+        with open(path) as fh:
+            doc = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha256") != kernel_source_digest() or doc.get("num_splits") != ns:
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, target_s: float):
+    """Time the fp64 oracle on a bounded sample of the workload: whole calls,
+    repeated until about target_s seconds, or a prefix of batch rows when one
+    call alone would take much longer."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.max_threads()
+    B = len(x.seq_lens)
+    rows = B
+    # probe with one batch row to size the sample
+    t = time.perf_counter()
+    oracle.attention(x.q[:1], x.k[:1], x.v[:1], x.seq_lens[:1], x.scale)
+    one = time.perf_counter() - t
+    per_row = max(one, 1e-4)
+    if per_row * B > 3 * target_s:
+        rows = max(1, int(target_s / per_row))
+    q, k, v, sl = x.q[:rows], x.k[:rows], x.v[:rows], x.seq_lens[:rows]
+    sample_bytes = int(sl.astype(np.int64).sum()) * x.k.shape[1] * x.k.shape[3] * 4
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.attention(q, k, v, sl, x.scale)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or calls >= 1000:
+            break
+    gbs = sample_bytes * calls / el / 1e9
+    sample = (f"{calls} oracle call(s) over {rows} of {B} batch row(s) "
+              f"({sample_bytes / 1e6:.1f} MB of K+V per call) in {el:.1f} s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "us_per_call": round(el / calls * 1e6 * B / rows, 1),
+            "cpu": cpu_model()}
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU: this build has no multi-GPU path "
+                         "(each GPU would run the same kernel on its own share of the "
+                         "sequences); run with --gpus 1.\n")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_split_amd as das
+    import workloads
+
+    das.load_library()
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[args.config]
+    x = workloads.config_inputs(args.config)
+    B, Hq, D = x.q.shape
+    Hkv, Smax = x.k.shape[1], x.k.shape[2]
+    kv_bytes = x.kv_bytes
+    ns, chunk = das.das_plan(B, Hkv, Hq // Hkv, Smax, D, args.splits)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = up(x.q)
+    sl = torch.from_numpy(x.seq_lens).to(dev)
+    alloc = x.k.nbytes + x.v.nbytes
+    copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
+    k0, v0 = up(x.k), up(x.v)
+    ks, vs = [k0], [v0]
+    for _ in range(copies - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(das.das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, args.splits), 16),
+                     dtype=torch.uint8, device=dev)   # zero-filled: starts with arrival counters
+
+    # One prepared decode-attention call per K/V copy.  It is a single kernel
+    # launch: phase 1 plus the fused phase-2 merge by the last workgroup of
+    # each (b, kv-head).
+    calls = [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
+                                args.splits, ws) for c in range(copies)]
+
+    for i in range(args.warmup):
+        calls[i % copies]()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_start = torch.cuda.Event(enable_timing=True)
+    ev_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_start.record()
+    for i in range(K):
+        calls[(args.warmup + i) % copies]()
+    ev_end.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # Each step is one kernel launch on this stream, so the events around the
+    # K back-to-back launches give that kernel's average launch duration.
+    kernel_ms = ev_start.elapsed_time(ev_end) / K
+    ms_per_step = elapsed / K * 1e3
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (kernel_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "description": cfg.description,
+            "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Smax": Smax,
+            "tokens": int(x.seq_lens.astype(np.int64).sum()),
+            "kv_bytes": kv_bytes,
+            "num_splits": ns, "chunk": chunk,
+            "out_dtype": args.out_dtype,
+            "kv_copies_rotated": copies,
+            "us_per_call": round(ms_per_step * 1e3, 2),
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_kv_decode",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(cfg.name, ns),
+            "kernel_us": round(kernel_ms * 1e3, 3),
+        },
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
