@@ -6,6 +6,7 @@
 // third grid axis cut into fixed-size chunks) and §6 "chunk size tuning guide"
 // (small chunks inflate the phase-2 traffic, large chunks leave compute units
 // idle; several times more blocks than compute units).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -20,15 +21,17 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_cache[kMaxDevices];
 
-// Workgroups per compute unit the automatic plan aims for.  One 8-wave
-// phase-1 workgroup is resident per CU, so one per CU keeps every split in a
-// single wave of workgroups, each long enough to stream efficiently.
-constexpr int64_t kTargetWgsPerCu = 1;
+// Workgroups the automatic plan aims for, per four compute units.  One
+// 8-wave phase-1 workgroup is resident per CU.  Measured on MI355X, about
+// three streaming workgroups per four CUs already saturate HBM, and the
+// fewer, longer splits cut the partial results and the per-workgroup start
+// and end latencies (32K-row GQA decode: 24 splits 28.5 us, 32 splits 30.7 us).
+constexpr int64_t kTargetWgsPer4Cus = 3;
 constexpr int64_t kMaxChunk = 8192;
 // Even when the batch alone fills the chip, a maximal-length sequence is cut
-// into at least this many splits: with variable lengths the last running
-// workgroups then hold at most a third of the longest sequence.
-constexpr int64_t kMinSplitsLongest = 3;
+// into at least this many splits, so that with variable lengths the last
+// running workgroups hold only a fifth of the longest sequence.
+constexpr int64_t kMinSplitsLongest = 5;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t q) { return ceil_div(a, q) * q; }
@@ -80,7 +83,7 @@ int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_
     const int rc = device_cus(num_cus, &cus);
     if (rc != DAS_OK) return rc;
     const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = kTargetWgsPerCu * cus;
+    const int64_t target = std::max<int64_t>(1, kTargetWgsPer4Cus * cus / 4);
     int64_t ns_fill = ceil_div(target, units);
     if (ns_fill < kMinSplitsLongest) ns_fill = kMinSplitsLongest;
     chunk = round_up(ceil_div(Smax, ns_fill), DAS_CHUNK_QUANTUM);

@@ -21,6 +21,9 @@ namespace das {
 #ifndef DAS_FUSED_FENCE
 #define DAS_FUSED_FENCE 0    // 1: agent-scope release fence before counting (L2 write-back)
 #endif
+#ifndef DAS_KV_CACHE_POLICY
+#define DAS_KV_CACHE_POLICY 2  // cache-policy bits of the K/V loads: nt (streamed once)
+#endif
 #ifndef DAS_MIN_WAVES_PER_EU
 #define DAS_MIN_WAVES_PER_EU 2  // occupancy the register allocator must allow
 #endif

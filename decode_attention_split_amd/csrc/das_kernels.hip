@@ -98,7 +98,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, DAS_KV_CACHE_POLICY);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
