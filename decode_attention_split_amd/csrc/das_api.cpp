@@ -32,6 +32,9 @@ constexpr int64_t kMaxChunk = 8192;
 // into at least this many splits, so that with variable lengths the last
 // running workgroups hold only a fifth of the longest sequence.
 constexpr int64_t kMinSplitsLongest = 5;
+// das_decode_attention fuses the merge into phase 1 up to this many split
+// workgroups per CU (see das_decode_attention below).
+constexpr int64_t kFusedWgsPerCu = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t q) { return ceil_div(a, q) * q; }
@@ -93,6 +96,12 @@ int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_
     const int64_t floor_chunk = round_up(ceil_div(Smax, DAS_MAX_SPLITS), DAS_CHUNK_QUANTUM);
     if (chunk < floor_chunk) chunk = floor_chunk;
   }
+#if DAS_ODD_CHUNK
+  // Splits that start at power-of-two multiples of a row stream through the
+  // same HBM channels in lockstep; an odd number of 128-row quanta staggers
+  // their start addresses.
+  if (chunk < Smax && (chunk / DAS_CHUNK_QUANTUM) % 2 == 0) chunk += DAS_CHUNK_QUANTUM;
+#endif
   const int64_t ns = ceil_div(Smax, chunk);
   if (ns < 1 || ns > DAS_MAX_SPLITS || chunk > INT32_MAX) return DAS_EINVAL;
   *ns_out = (int32_t)ns;
@@ -131,6 +140,9 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   if (!std::isfinite(scale)) return DAS_EINVAL;
   const int32_t G = Hq / Hkv;
   if (!supported_dims(D, G)) return DAS_ENOTSUP;
+  // a sequence's K (or V) rows, plus one tile of overhang, are addressed
+  // with 32-bit byte offsets
+  if ((int64_t)(Smax + 256) * D * 2 > INT32_MAX) return DAS_ENOTSUP;
   if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
   if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
   int32_t ns = 0, chunk = 0;
@@ -146,6 +158,13 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   return DAS_OK;
 }
 
+// Rows per block a split streams: the whole chunk, or (interleaved plans)
+// one block of kWaves * kTile rows per step, split s taking blocks s, s+ns, ...
+int32_t block_rows(const Checked& c) {
+  if (DAS_INTERLEAVE && c.ns > 1) return das::kWaves * das::kTile;
+  return c.chunk;
+}
+
 int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out,
                int32_t out_dtype, float* lse_out, void* workspace, const Checked& c, bool fused,
@@ -158,7 +177,7 @@ int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_l
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.Smax = Smax;
-  a.chunk = c.chunk;
+  a.chunk = block_rows(c);
   a.ns = c.ns;
   a.scale_log2e = scale * 1.44269504088896341f;
   a.direct = c.ns == 1;
@@ -172,7 +191,12 @@ int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_l
   a.out = out;
   a.lse = lse_out;
   a.out_bf16 = out_dtype == DAS_BF16;
-  return das::launch_split_kv_decode(D, c.G, B, a, st) == hipSuccess ? DAS_OK : DAS_ELAUNCH;
+  // At most one workgroup per CU when there are no more workgroups than CUs.
+  int cus = 0;
+  if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
+  const bool one_per_cu = DAS_ONE_PER_CU && (int64_t)B * Hkv * c.ns <= cus;
+  return das::launch_split_kv_decode(D, c.G, B, a, one_per_cu, st) == hipSuccess ? DAS_OK
+                                                                                 : DAS_ELAUNCH;
 }
 
 int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int32_t D,
@@ -186,7 +210,7 @@ int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int
   a.ws_ml = reinterpret_cast<const float*>(ws + ws_ml_offset(B, Hq, c.ns, D));
   a.Hq = Hq;
   a.Smax = Smax;
-  a.chunk = c.chunk;
+  a.chunk = block_rows(c);
   a.ns = c.ns;
   a.out = out;
   a.lse = lse_out;
@@ -249,9 +273,16 @@ int das_decode_attention(const void* q, const void* k_cache, const void* v_cache
   if (rc != DAS_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One launch: the last workgroup of each (b, kv-head) merges the splits.
-  // Shapes with more (b, kv-head) pairs than counter slots run the merge as
-  // a second kernel instead.
-  const bool fused = (int64_t)B * Hkv <= das::kCounterSlots;
+  // Every split workgroup then ends with a store-completion wait and a
+  // counter round trip while it holds its CU; with many more workgroups than
+  // CUs that costs more than a second, small merge kernel (B=64 varlen
+  // decode, 2560 workgroups: 375 us fused, 363 us as two kernels), so the
+  // merge is fused only up to kFusedWgsPerCu workgroups per CU.  Shapes with
+  // more (b, kv-head) pairs than counter slots always use the second kernel.
+  int cus = 0;
+  if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
+  const bool fused = (int64_t)B * Hkv <= das::kCounterSlots &&
+                     (int64_t)B * Hkv * c.ns <= kFusedWgsPerCu * cus;
   const int rc1 = run_phase1(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
                              out_dtype, lse_out, workspace, c, fused, st);
   if (rc1 != DAS_OK || fused) return rc1;

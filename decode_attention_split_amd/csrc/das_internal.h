@@ -15,8 +15,8 @@ namespace das {
 #ifndef DAS_TILE
 #define DAS_TILE 32          // K/V rows a wave handles per loop iteration (16 or 32)
 #endif
-#ifndef DAS_PREFETCH
-#define DAS_PREFETCH 0       // 1: load the next tile into registers while computing this one
+#ifndef DAS_INTERLEAVE
+#define DAS_INTERLEAVE 0     // 1: splits own interleaved 256-row blocks instead of one chunk
 #endif
 #ifndef DAS_FUSED_FENCE
 #define DAS_FUSED_FENCE 0    // 1: agent-scope release fence before counting (L2 write-back)
@@ -24,8 +24,17 @@ namespace das {
 #ifndef DAS_KV_CACHE_POLICY
 #define DAS_KV_CACHE_POLICY 2  // cache-policy bits of the K/V loads: nt (streamed once)
 #endif
+#ifndef DAS_ODD_CHUNK
+#define DAS_ODD_CHUNK 0      // 1: chunks are odd multiples of the 128-row quantum
+#endif
+#ifndef DAS_ONE_PER_CU
+#define DAS_ONE_PER_CU 1     // 1: grids of at most one workgroup per CU are spread one per CU
+#endif
 #ifndef DAS_MIN_WAVES_PER_EU
-#define DAS_MIN_WAVES_PER_EU 2  // occupancy the register allocator must allow
+#define DAS_MIN_WAVES_PER_EU 2  // occupancy the register allocator must allow (G = 2, 8)
+#endif
+#ifndef DAS_MIN_WAVES_PER_EU_SMALL_G
+#define DAS_MIN_WAVES_PER_EU_SMALL_G 4  // G = 1, 4: two 8-wave workgroups per CU
 #endif
 
 constexpr int kWaves = DAS_WAVES;
@@ -41,7 +50,7 @@ struct SplitArgs {
   const uint16_t* v;         // bf16 [B][Hkv][Smax][D]
   const int32_t* seq_lens;   // int32 [B]
   int32_t Hq, Hkv, Smax;
-  int32_t chunk, ns;         // rows per split, number of splits
+  int32_t chunk, ns;         // rows per block (split s owns blocks s, s+ns, ...), splits
   float scale_log2e;         // scale * log2(e): logits are kept in base-2 units
   float* ws_o;               // [B][Hq][ns][D] unnormalised partial outputs
   float* ws_ml;              // [B][Hq][ns][2] (split max in base-2 units, exp2 sum)
@@ -63,7 +72,7 @@ struct CombineArgs {
   const int32_t* seq_lens;
   const float* ws_o;
   const float* ws_ml;
-  int32_t Hq, Smax, chunk, ns;
+  int32_t Hq, Smax, chunk, ns;   // chunk: rows per block, as in SplitArgs
   void* out;
   float* lse;                // may be null
   int32_t out_bf16;
@@ -81,7 +90,13 @@ struct MergeArgs {
   int32_t bf16;
 };
 
-hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, hipStream_t stream);
+// LDS per workgroup and per CU on gfx950 is 160 KiB.  A phase-1 workgroup
+// that asks for kOnePerCuLds in total (static + dynamic) leaves no room for
+// a second one on its CU.
+constexpr int kMaxLdsPerWorkgroup = 160 * 1024;
+constexpr int kOnePerCuLds = 84 * 1024;
+hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
+                                  hipStream_t stream);
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
 hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t stream);
 

@@ -157,17 +157,35 @@ __device__ __forceinline__ void store_out4(const SplitArgs& a, size_t e, float x
   }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Static LDS of split_kv_decode<D, G>: per wave a K tile and a p buffer,
+// reused at the end for the wave merge.
+template <int D, int G>
+constexpr int split_smem_bytes() {
+  constexpr int kWaveBytes = kTile * 2 * D + kTile * G * 4;
+  constexpr int kMergeBytes = (G * D + 2 * G) * 4;
+  return kWaves * (kWaveBytes > kMergeBytes ? kWaveBytes : kMergeBytes);
+}
+
 // ---------------------------------------------------------------------------
-// Phase 1: split_kv_decode.  Grid (ns, Hkv, B), kThreads threads.
+// Phase 1: split_kv_decode.  Grid (ns | 1, Hkv, B), kThreads threads.
 // ---------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decode_kernel(SplitArgs a) {
+__global__ __launch_bounds__(kThreads, (G == 1 || G == 4) ? DAS_MIN_WAVES_PER_EU_SMALL_G
+                                                       : DAS_MIN_WAVES_PER_EU)
+    void split_kv_decode_kernel(SplitArgs a) {
   constexpr int kLanesPerRow = D / 8;           // lanes covering one K/V row, 16 B each
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kTile / kRowsPerLoad;  // 16-byte loads per lane per tile (K or V)
@@ -176,32 +194,43 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
   constexpr int kPBytes = kTile * G * 4;
   constexpr int kWaveBytes = kKTileBytes + kPBytes;
   constexpr int kMergeBytes = (G * D + 2 * G) * 4;
-  constexpr int kSmemBytes =
-      kWaves * (kWaveBytes > kMergeBytes ? kWaveBytes : kMergeBytes);
+  constexpr int kSmemBytes = split_smem_bytes<D, G>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
+  static_assert(kKTileBytes == kLoads * 1024, "one 1 KiB LDS slab per K load");
   static_assert((kThreads > G * D / 4 ? kThreads : G * D / 4) * 16 + kThreads * 4 +
                         kWaves * G * 4 <= kSmemBytes,
                 "fused merge scratch must fit in the tile LDS");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
+  // Grid (ns rounded up to odd, Hkv, B).  Workgroups are dealt to the eight
+  // XCDs in linear-id order; an odd split extent keeps split s of every
+  // sequence from always landing on the same XCD (when ns is a multiple of
+  // 8, every sequence's first split would share XCD 0).  The padding splits
+  // exit at once.
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (s >= a.ns) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int L = clamp_len(a.seq_lens[b], a.Smax);
-  const int j0 = s * a.chunk;
-  const int j1 = min(j0 + a.chunk, L);
+  // The sequence's rows are cut into blocks of a.chunk rows; split s owns
+  // blocks s, s + ns, s + 2*ns, ...  (one block per split when the block is
+  // the whole chunk ceil(Smax/ns)).
+  const int nb = (L + a.chunk - 1) / a.chunk;   // blocks holding valid rows
+  const int nsb = min(a.ns, nb);                // splits this sequence uses
   // An empty split exits at once; phase 2 never reads it.  With the fused
   // merge, split 0 of an empty sequence stays to write out = 0, lse = -inf.
-  if (!a.direct && j0 >= L && !(a.fused && s == 0)) return;
-  const int n_rows = j1 > j0 ? j1 - j0 : 0;
+  if (!a.direct && s >= nb && !(a.fused && s == 0)) return;
 
   unsigned char* kt = smem + wave * kWaveBytes;
   float* pt = reinterpret_cast<float*>(kt + kKTileBytes);
 
-  // This split's rows of K and V, as bounds-checked buffers.
-  const size_t slab = (((size_t)b * a.Hkv + g) * (size_t)a.Smax + (size_t)j0) * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + slab, n_rows * kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + slab, n_rows * kRowBytes);
+  // The sequence's valid rows of K and V as bounds-checked buffers: loads
+  // past row L return zeros, and the rows beyond seq_lens are never read.
+  const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + slab, L * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + slab, L * kRowBytes);
+  int row_end = 0;                              // end of the block being streamed
   const int row_in_load = lane / kLanesPerRow;  // this lane's row within a load
   const int chunk = lane % kLanesPerRow;        // this lane's 16-byte chunk of a row
   const int lane_off = row_in_load * kRowBytes + 16 * chunk;
@@ -258,21 +287,29 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
 #pragma unroll
   for (int i = 0; i < kLaneHeads; ++i) l_lane[i] = 0.f;
 
-  auto load_tile = [&](int r0, uint4* kr, uint4* vr) {
+  // K goes from HBM straight into the wave's LDS tile (buffer_load ... lds):
+  // load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the tile, lane l the
+  // 16 bytes at 16*l, i.e. row kRowsPerLoad*m + row_in_load, slot `chunk`.
+  // The lane fetches the logical chunk whose swizzled slot that is, so the
+  // tile ends up in the k_tile_offset layout.  V goes to registers.
+  auto load_tile = [&](int r0, uint4* vr) {
     const int soff = r0 * kRowBytes;
 #pragma unroll
     for (int m = 0; m < kLoads; ++m) {
-      const int voff = lane_off + m * kRowsPerLoad * kRowBytes;
-      kr[m] = buffer_load16(rk, voff, soff);
-      vr[m] = buffer_load16(rv, voff, soff);
+      const int r = kRowsPerLoad * m + row_in_load;
+      const int c = chunk ^ ((r / (256 / kRowBytes)) % kLanesPerRow);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(kt + m * 1024), 16,
+          r * kRowBytes + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
     }
-  };
-
-  auto process_tile = [&](int r0, const uint4* kr, const uint4* vr) {
-    // stage K through LDS (swizzled)
 #pragma unroll
     for (int m = 0; m < kLoads; ++m)
-      *reinterpret_cast<uint4*>(kt + k_tile_offset<D>(kRowsPerLoad * m + row_in_load, chunk)) = kr[m];
+      vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+  };
+
+  auto process_tile = [&](int r0, const uint4* vr) {
+    // the K loads were issued before the V loads: wait for them only
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
     wave_lds_fence();
 
     float alpha[G];
@@ -291,7 +328,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
               kt + k_tile_offset<D>(16 * tg + n, 4 * kb + (lane >> 4)));
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], as_bf16x8(kw), sacc, 0, 0, 0);
         }
-        const bool ok = r0 + 16 * tg + n < n_rows;
+        const bool ok = r0 + 16 * tg + n < row_end;
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[tg][r] = ok ? sacc[r] * c2 : -INFINITY;
       }
@@ -352,7 +389,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
             x[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[h][4 * cc + i]), as_bf16x2(kwv[i]),
                                                    x[h], false);
       }
-      const bool ok = r0 + n < n_rows;
+      const bool ok = r0 + n < row_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -415,28 +452,13 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
   };
 
   const int stride = kWaves * kTile;
-  if constexpr (DAS_PREFETCH) {
-    int r0 = wave * kTile;
-    if (r0 < n_rows) {
-      uint4 ka[kLoads], va[kLoads], kb_[kLoads], vb[kLoads];
-      load_tile(r0, ka, va);
-      while (true) {
-        const int r1 = r0 + stride;
-        if (r1 < n_rows) load_tile(r1, kb_, vb);
-        process_tile(r0, ka, va);
-        if (r1 >= n_rows) break;
-        const int r2 = r1 + stride;
-        if (r2 < n_rows) load_tile(r2, ka, va);
-        process_tile(r1, kb_, vb);
-        if (r2 >= n_rows) break;
-        r0 = r2;
-      }
-    }
-  } else {
-    for (int r0 = wave * kTile; r0 < n_rows; r0 += stride) {
-      uint4 kr[kLoads], vr[kLoads];
-      load_tile(r0, kr, vr);
-      process_tile(r0, kr, vr);
+  for (int blk = s; blk < nb; blk += a.ns) {
+    const int row_lo = blk * a.chunk;
+    row_end = min(row_lo + a.chunk, L);
+    for (int r0 = row_lo + wave * kTile; r0 < row_end; r0 += stride) {
+      uint4 vr[kLoads];
+      load_tile(r0, vr);
+      process_tile(r0, vr);
     }
   }
 
@@ -487,7 +509,6 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
 
   // A sequence that uses at most one split is finished by split 0's
   // workgroup; so is every sequence of a single-split plan.
-  const int nsb = (L + a.chunk - 1) / a.chunk;
   const bool finish_here = a.direct || (a.fused && nsb <= 1);
   constexpr int kQuads = D / 4;                 // float4 quads per output row
   // Partials of this (b, kv-head): rows (head, split) of D floats, and
@@ -562,35 +583,8 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
   constexpr int kPerRound = kThreads / kGroups;
   float4* red4 = reinterpret_cast<float4*>(smem);                        // [kGroups][kPairs]
   float* redl = reinterpret_cast<float*>(smem + kGroups * kPairs * 16);  // [kGroups][G]
-  float* redm = redl + kGroups * G;                                      // [kWaves][G]
-
-  // global max of every head over its splits: strided pass + block reduction
-  float mloc[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) mloc[hh] = -INFINITY;
-  for (int i = tid; i < G * nsb; i += kThreads) {
-    const int hi = i / nsb, c = i - hi * nsb;
-    const float m = coherent_load8(rml, (hi * a.ns + c) * 8).x;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      if (hh == hi) mloc[hh] = fmaxf(mloc[hh], m);
-  }
+  float* redm = redl + kGroups * G;                                      // [kGroups][G]
   __syncthreads();  // the wave-merge reads of the LDS are done
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float v = row_reduce16<true>(mloc[hh]);
-    const float wmax = fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
-                             fmaxf(lane_value(v, 32), lane_value(v, 48)));
-    if (lane == 0) redm[wave * G + hh] = wmax;
-  }
-  __syncthreads();
-  float Mh[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    Mh[hh] = redm[hh];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) Mh[hh] = fmaxf(Mh[hh], redm[w * G + hh]);
-  }
 
   for (int pair0 = 0; pair0 < kPairs; pair0 += kPerRound) {
     const int pair = pair0 + tid % kPerRound;
@@ -598,14 +592,12 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
     const bool active = pair < kPairs;
     const int h = active ? pair / kQuads : 0, quad = active ? pair % kQuads : 0;
     const size_t qh = qh0 + h;
-    float M = Mh[0];
-#pragma unroll
-    for (int hh = 1; hh < G; ++hh)
-      if (hh == h) M = Mh[hh];
+    // This thread's splits, merged online: batches of 8 loaded in one round
+    // trip, the running sums rescaled when a batch raises the running max.
+    float mt = -INFINITY;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float ls = 0.f;
     if (active) {
-      // issue the loads of up to 8 splits before using any of them
       constexpr int kBatch = 8;
       for (int c0 = grp; c0 < nsb; c0 += kBatch * kGroups) {
         float2 st[kBatch];
@@ -621,35 +613,53 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU) void split_kv_decod
             u[k] = make_float4(0.f, 0.f, 0.f, 0.f);
           }
         }
+        float bm = st[0].x;
+#pragma unroll
+        for (int k = 1; k < kBatch; ++k) bm = fmaxf(bm, st[k].x);
+        const float mn = fmaxf(mt, bm);  // finite: split c0 < nsb is in the batch
+        const float alpha = fast_exp2(mt - mn);
+        o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
+        ls *= alpha;
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-          const float w = fast_exp2(st[k].x - M);  // 0 for the padding slots
+          const float w = fast_exp2(st[k].x - mn);  // 0 for the padding slots
           o.x = fmaf(w, u[k].x, o.x);
           o.y = fmaf(w, u[k].y, o.y);
           o.z = fmaf(w, u[k].z, o.z);
           o.w = fmaf(w, u[k].w, o.w);
           ls = fmaf(w, st[k].y, ls);
         }
+        mt = mn;
       }
     }
-    __syncthreads();  // the LDS is free again (previous round or the wave merge)
     if (active) {
       red4[grp * kPairs + pair] = o;
-      if (quad == 0) redl[grp * G + h] = ls;
+      if (quad == 0) {
+        redl[grp * G + h] = ls;
+        redm[grp * G + h] = mt;
+      }
     }
     __syncthreads();
     if (active && grp == 0) {
-      float4 t = o;
+      float M = redm[h];
+      for (int gi = 1; gi < kGroups; ++gi) M = fmaxf(M, redm[gi * G + h]);
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
       float lt = 0.f;
-      for (int gi = 0; gi < kGroups; ++gi) lt += redl[gi * G + h];
-      for (int gi = 1; gi < kGroups; ++gi) {
+      for (int gi = 0; gi < kGroups; ++gi) {
+        const float mg = redm[gi * G + h];
+        const float f = (mg == -INFINITY) ? 0.f : fast_exp2(mg - M);
         const float4 u = red4[gi * kPairs + pair];
-        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        t.x = fmaf(f, u.x, t.x);
+        t.y = fmaf(f, u.y, t.y);
+        t.z = fmaf(f, u.z, t.z);
+        t.w = fmaf(f, u.w, t.w);
+        lt = fmaf(f, redl[gi * G + h], lt);
       }
       const float inv = 1.f / lt;
       store_out4(a, qh * D + 4 * quad, t.x * inv, t.y * inv, t.z * inv, t.w * inv);
       if (quad == 0 && a.lse != nullptr) a.lse[qh] = (M + __log2f(lt)) * kLn2;
     }
+    __syncthreads();  // before the next round reuses the LDS
   }
 }
 
@@ -690,7 +700,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int quad = tid % kQuads, grp = tid / kQuads;
   const int L = clamp_len(a.seq_lens[b], a.Smax);
-  const int nsb = (L + a.chunk - 1) / a.chunk;  // splits this sequence used
+  const int nsb = min(a.ns, (L + a.chunk - 1) / a.chunk);  // splits this sequence used
   const size_t qh = (size_t)b * a.Hq + h;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml + qh * a.ns * 2);
   const float4* po = reinterpret_cast<const float4*>(a.ws_o + qh * a.ns * D) + quad;
@@ -817,26 +827,46 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 template <int D, int G>
-static hipError_t launch_split(int B, const SplitArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)a.ns, (unsigned)a.Hkv, (unsigned)B);
-  hipLaunchKernelGGL((split_kv_decode_kernel<D, G>), grid, dim3(kThreads), 0, st, a);
+static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipStream_t st) {
+  // Dynamic LDS that brings the workgroup's total to kOnePerCuLds, more than
+  // half a CU's LDS, so no second workgroup fits on the CU; a grid with no
+  // more workgroups than CUs then spreads over all of them instead of
+  // doubling up on some.  The static part already counts toward the total.
+  constexpr int kStatic = split_smem_bytes<D, G>() + 64;  // + small scalars
+  static_assert(kStatic + 0 <= kMaxLdsPerWorkgroup, "static LDS over the limit");
+  constexpr int kPad = kStatic < kOnePerCuLds ? kOnePerCuLds - kStatic : 0;
+  static_assert(kStatic + kPad <= kMaxLdsPerWorkgroup, "padded LDS over the limit");
+  // The compiled kernel's own static LDS, read once: the pad is dropped (a
+  // pure placement hint) if static + pad would not fit in a workgroup.
+  static const int static_lds = [] {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&split_kv_decode_kernel<D, G>)) !=
+        hipSuccess)
+      return -1;
+    return (int)fa.sharedSizeBytes;
+  }();
+  const bool pad_fits = static_lds >= 0 && static_lds + kPad <= kMaxLdsPerWorkgroup;
+  dim3 grid((unsigned)(a.ns | 1), (unsigned)a.Hkv, (unsigned)B);
+  hipLaunchKernelGGL((split_kv_decode_kernel<D, G>), grid, dim3(kThreads),
+                     (unsigned)(one_per_cu && pad_fits ? kPad : 0), st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, hipStream_t st) {
+hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
+                                  hipStream_t st) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch_split<128, 1>(B, a, st);
-      case 2: return launch_split<128, 2>(B, a, st);
-      case 4: return launch_split<128, 4>(B, a, st);
-      case 8: return launch_split<128, 8>(B, a, st);
+      case 1: return launch_split<128, 1>(B, a, one_per_cu, st);
+      case 2: return launch_split<128, 2>(B, a, one_per_cu, st);
+      case 4: return launch_split<128, 4>(B, a, one_per_cu, st);
+      case 8: return launch_split<128, 8>(B, a, one_per_cu, st);
     }
   } else if (D == 64) {
     switch (G) {
-      case 1: return launch_split<64, 1>(B, a, st);
-      case 2: return launch_split<64, 2>(B, a, st);
-      case 4: return launch_split<64, 4>(B, a, st);
-      case 8: return launch_split<64, 8>(B, a, st);
+      case 1: return launch_split<64, 1>(B, a, one_per_cu, st);
+      case 2: return launch_split<64, 2>(B, a, one_per_cu, st);
+      case 4: return launch_split<64, 4>(B, a, one_per_cu, st);
+      case 8: return launch_split<64, 8>(B, a, one_per_cu, st);
     }
   }
   return hipErrorInvalidValue;

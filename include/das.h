@@ -40,7 +40,8 @@
  *   - Calls are re-entrant.  Concurrent calls must not share a workspace.
  *   - Supported shapes: head dim D in {64, 128}; GQA group G = Hq / Hkv in
  *     {1, 2, 4, 8} (Hq a multiple of Hkv); 1 <= B <= 65535; 1 <= Hkv <= 65535;
- *     1 <= Smax; num_splits <= DAS_MAX_SPLITS.
+ *     1 <= Smax with (Smax + 256) * D * 2 < 2^31 (one sequence's K rows are
+ *     addressed with 32-bit byte offsets); num_splits <= DAS_MAX_SPLITS.
  *   - Query head h reads kv-head h / G.
  *   - Device-side precondition (not checked on the host, since reading
  *     seq_lens would need a device-to-host copy): 0 <= seq_lens[b] <= Smax.
@@ -123,8 +124,10 @@ size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Sm
  * (phase 1); the last workgroup of each (b, kv-head) to finish, found with a
  * device-scope arrival counter in the workspace, merges every split of that
  * kv-head (phase 2).  A sequence that uses one split, and every sequence of
- * a single-split plan, is written directly by its workgroup.  (Shapes with
- * more than 65536 (b, kv-head) pairs run phase 2 as a second kernel.)
+ * a single-split plan, is written directly by its workgroup.  When the plan
+ * has more than 4 split workgroups per compute unit (B*Hkv*NS > 4*CUs), or
+ * more than 65536 (b, kv-head) pairs, phase 2 runs as a second kernel
+ * instead (as das_lse_combine).
  * Workspace precondition: its first DAS_WORKSPACE_COUNTER_BYTES must be zero
  * before the workspace is first used (allocate it zero-filled); every
  * completed call leaves them zero again, whatever the shape.

@@ -139,3 +139,17 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out, eager_o) and torch.equal(lse, eager_l), f"replay {i}"
         _ = (torch.ones(1000, device=dev()) * 2).sum().item()   # eager work between replays
     note("graph replays match eager")
+
+
+def test_many_split_workgroups_take_the_two_kernel_merge():
+    """B*Hkv*NS above 4 workgroups per CU: das_decode_attention merges with a
+    second kernel instead of the fused last-workgroup merge; same results."""
+    cfg = workloads.custom_config(16, 32, 8, 128, 2048)
+    lens = [2048, 1, 0, 777, 2047, 1500, 128, 129, 1024, 2000, 5, 1800, 256, 900, 1999, 64]
+    x = workloads.make_inputs(cfg, 8, seq_lens=lens)
+    q, k, v, sl = upload(x)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    for ns in (16, 9):   # 16*8*16 = 2048 and 16*8*9 = 1152 split workgroups
+        out, lse = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns)
+        torch.cuda.synchronize()
+        check_f32(out, lse, *ref, f"two-kernel merge ns={ns}")

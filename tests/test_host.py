@@ -125,6 +125,7 @@ def _call_decode(lib, **kw):
     (dict(scale=float("nan")), das.DAS_EINVAL), (dict(q=24), das.DAS_EINVAL),
     (dict(ws=0), das.DAS_EWORKSPACE), (dict(wsb=100), das.DAS_EWORKSPACE),
     (dict(ns=das.DAS_MAX_SPLITS + 1), das.DAS_EINVAL),
+    (dict(Smax=(1 << 23)), das.DAS_ENOTSUP),        # 32-bit row offsets per sequence
 ])
 def test_decode_argument_checks(lib, kw, status):
     # All pointers are fake: a failed check must return before any launch.
