@@ -31,10 +31,7 @@ namespace das {
 #define DAS_ONE_PER_CU 1     // 1: grids of at most one workgroup per CU are spread one per CU
 #endif
 #ifndef DAS_MIN_WAVES_PER_EU
-#define DAS_MIN_WAVES_PER_EU 2  // occupancy the register allocator must allow (G = 2, 8)
-#endif
-#ifndef DAS_MIN_WAVES_PER_EU_SMALL_G
-#define DAS_MIN_WAVES_PER_EU_SMALL_G 4  // G = 1, 4: two 8-wave workgroups per CU
+#define DAS_MIN_WAVES_PER_EU 2  // waves per SIMD the register allocator must allow
 #endif
 
 constexpr int kWaves = DAS_WAVES;

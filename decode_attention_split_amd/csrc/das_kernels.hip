@@ -28,8 +28,8 @@
 //   * The online softmax keeps, per wave and head, a running max (base-2
 //     units: logits are scaled by scale*log2(e) in fp32 after the dot) and
 //     rescales the partial sums only when the max grows.
-//   * The four waves of a workgroup merge their states through LDS at the
-//     end; the workgroup then writes its split's (o, m, l) partial, or, for a
+//   * The waves of a workgroup merge their states through LDS at the end;
+//     the workgroup then writes its split's (o, m, l) partial, or, for a
 //     single-split plan, the final output.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -183,8 +183,7 @@ constexpr int split_smem_bytes() {
 // Phase 1: split_kv_decode.  Grid (ns | 1, Hkv, B), kThreads threads.
 // ---------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, (G == 1 || G == 4) ? DAS_MIN_WAVES_PER_EU_SMALL_G
-                                                       : DAS_MIN_WAVES_PER_EU)
+__global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     void split_kv_decode_kernel(SplitArgs a) {
   constexpr int kLanesPerRow = D / 8;           // lanes covering one K/V row, 16 B each
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
@@ -520,27 +519,31 @@ __global__ __launch_bounds__(kThreads, (G == 1 || G == 4) ? DAS_MIN_WAVES_PER_EU
       make_rsrc(a.ws_ml + (a.direct ? 0 : qh0 * a.ns * 2), G * a.ns * 2 * 4);
   for (int idx = tid; idx < G * kQuads; idx += kThreads) {
     const int h = idx / kQuads, quad = idx % kQuads;
-    float mw[kWaves], M = -INFINITY;
+    // every wave's state is read before any of it is used, so the LDS
+    // reads overlap instead of taking one round trip per wave
+    float mw[kWaves], lw[kWaves];
+    float4 uw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* mgw = reinterpret_cast<const float*>(smem + w * kMergeBytes);
       mw[w] = mgw[G * D + h];
-      M = fmaxf(M, mw[w]);
+      lw[w] = mgw[G * D + G + h];
+      uw[w] = *reinterpret_cast<const float4*>(mgw + h * D + 4 * quad);
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+    // a wave that saw no row (max -inf) weighs 0; so does every wave when M = -inf
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float lsum = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* mgw = reinterpret_cast<const float*>(smem + w * kMergeBytes);
-        const float f = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
-        const float4 u = *reinterpret_cast<const float4*>(mgw + h * D + 4 * quad);
-        o.x = fmaf(f, u.x, o.x);
-        o.y = fmaf(f, u.y, o.y);
-        o.z = fmaf(f, u.z, o.z);
-        o.w = fmaf(f, u.w, o.w);
-        lsum = fmaf(f, mgw[G * D + G + h], lsum);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+      o.x = fmaf(f, uw[w].x, o.x);
+      o.y = fmaf(f, uw[w].y, o.y);
+      o.z = fmaf(f, uw[w].z, o.z);
+      o.w = fmaf(f, uw[w].w, o.w);
+      lsum = fmaf(f, lw[w], lsum);
     }
     const size_t qh = qh0 + h;
     if (finish_here) {
