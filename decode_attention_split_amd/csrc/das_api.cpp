@@ -96,12 +96,6 @@ int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_
     const int64_t floor_chunk = round_up(ceil_div(Smax, DAS_MAX_SPLITS), DAS_CHUNK_QUANTUM);
     if (chunk < floor_chunk) chunk = floor_chunk;
   }
-#if DAS_ODD_CHUNK
-  // Splits that start at power-of-two multiples of a row stream through the
-  // same HBM channels in lockstep; an odd number of 128-row quanta staggers
-  // their start addresses.
-  if (chunk < Smax && (chunk / DAS_CHUNK_QUANTUM) % 2 == 0) chunk += DAS_CHUNK_QUANTUM;
-#endif
   const int64_t ns = ceil_div(Smax, chunk);
   if (ns < 1 || ns > DAS_MAX_SPLITS || chunk > INT32_MAX) return DAS_EINVAL;
   *ns_out = (int32_t)ns;
@@ -160,11 +154,6 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
 
 // Rows per block a split streams: the whole chunk, or (interleaved plans)
 // one block of kWaves * kTile rows per step, split s taking blocks s, s+ns, ...
-int32_t block_rows(const Checked& c) {
-  if (DAS_INTERLEAVE && c.ns > 1) return das::kWaves * das::kTile;
-  return c.chunk;
-}
-
 int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out,
                int32_t out_dtype, float* lse_out, void* workspace, const Checked& c, bool fused,
@@ -177,7 +166,7 @@ int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_l
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.Smax = Smax;
-  a.chunk = block_rows(c);
+  a.chunk = c.chunk;
   a.ns = c.ns;
   a.scale_log2e = scale * 1.44269504088896341f;
   a.direct = c.ns == 1;
@@ -210,7 +199,7 @@ int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int
   a.ws_ml = reinterpret_cast<const float*>(ws + ws_ml_offset(B, Hq, c.ns, D));
   a.Hq = Hq;
   a.Smax = Smax;
-  a.chunk = block_rows(c);
+  a.chunk = c.chunk;
   a.ns = c.ns;
   a.out = out;
   a.lse = lse_out;

@@ -15,17 +15,8 @@ namespace das {
 #ifndef DAS_TILE
 #define DAS_TILE 32          // K/V rows a wave handles per loop iteration (16 or 32)
 #endif
-#ifndef DAS_INTERLEAVE
-#define DAS_INTERLEAVE 0     // 1: splits own interleaved 256-row blocks instead of one chunk
-#endif
-#ifndef DAS_FUSED_FENCE
-#define DAS_FUSED_FENCE 0    // 1: agent-scope release fence before counting (L2 write-back)
-#endif
 #ifndef DAS_KV_CACHE_POLICY
 #define DAS_KV_CACHE_POLICY 2  // cache-policy bits of the K/V loads: nt (streamed once)
-#endif
-#ifndef DAS_ODD_CHUNK
-#define DAS_ODD_CHUNK 0      // 1: chunks are odd multiples of the 128-row quantum
 #endif
 #ifndef DAS_ONE_PER_CU
 #define DAS_ONE_PER_CU 1     // 1: grids of at most one workgroup per CU are spread one per CU
@@ -47,7 +38,7 @@ struct SplitArgs {
   const uint16_t* v;         // bf16 [B][Hkv][Smax][D]
   const int32_t* seq_lens;   // int32 [B]
   int32_t Hq, Hkv, Smax;
-  int32_t chunk, ns;         // rows per block (split s owns blocks s, s+ns, ...), splits
+  int32_t chunk, ns;         // rows per split, splits
   float scale_log2e;         // scale * log2(e): logits are kept in base-2 units
   float* ws_o;               // [B][Hq][ns][D] unnormalised partial outputs
   float* ws_ml;              // [B][Hq][ns][2] (split max in base-2 units, exp2 sum)

@@ -563,12 +563,11 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   // ---- fused phase 2: the last workgroup of this (b, kv-head) to arrive
   // merges every split's partial (FlashDecoding++ post, §3 phase 2) ----
   __shared__ int s_last;
-  // This workgroup's partial stores must be complete before it is counted.
-#if DAS_FUSED_FENCE
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-#else
+  // This workgroup's partial stores must be complete before it is counted:
+  // a store becomes visible to another XCD only about when its
+  // acknowledgement arrives, so waiting for it here costs no more than the
+  // merging workgroup would otherwise spend waiting for the data.
   __builtin_amdgcn_s_waitcnt(0);
-#endif
   __syncthreads();
   if (tid == 0) {
     unsigned int* cnt = a.counters + (size_t)b * a.Hkv + g;

@@ -153,3 +153,46 @@ def test_many_split_workgroups_take_the_two_kernel_merge():
         out, lse = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns)
         torch.cuda.synchronize()
         check_f32(out, lse, *ref, f"two-kernel merge ns={ns}")
+
+
+def test_fused_merge_ignores_whatever_the_partial_slots_held():
+    """The fused merge reads a split's slot only once this call has written it:
+    every split clears its slots before it is counted.  Garbage, another
+    input's partials (left by the phase-1 entry point) or another shape's
+    leftovers in the partial area never reach the result."""
+    cfg = workloads.custom_config(2, 32, 8, 128, 5000)
+    x = workloads.make_inputs(cfg, 10, seq_lens=(5000, 3100))
+    y = workloads.make_inputs(cfg, 11, seq_lens=(4900, 5000))
+    qx, kx, vx, slx = upload(x)
+    qy, ky, vy, sly = upload(y)
+    ns = 9
+    need = das.das_decode_workspace_bytes(2, 32, 8, 5000, 128, ns)
+    clean = torch.zeros(need, dtype=torch.uint8, device=dev())
+    want_o, want_l = das.das_decode_attention(qx, kx, vx, slx, x.scale, num_splits=ns,
+                                              workspace=clean)
+    torch.cuda.synchronize()
+    check_f32(want_o, want_l, *oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale),
+              "fused merge, clean workspace")
+
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    cb = das.DAS_WORKSPACE_COUNTER_BYTES
+    g = torch.Generator(device="cpu").manual_seed(3)
+    junk = torch.randint(1, 255, (need - cb,), dtype=torch.uint8, generator=g)
+    ws[cb:] = junk.to(dev())                                   # garbage, no zero byte
+    got = das.das_decode_attention(qx, kx, vx, slx, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], want_o) and torch.equal(got[1], want_l), "after garbage"
+
+    # another input's partials, written by the phase-1 entry point and never merged
+    das.das_split_kv_decode(qy, ky, vy, sly, y.scale, num_splits=ns, workspace=ws)
+    got = das.das_decode_attention(qx, kx, vx, slx, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], want_o) and torch.equal(got[1], want_l), "after phase-1 leftovers"
+
+    # a different split count puts other shapes' slots over these ones
+    das.das_split_kv_decode(qy, ky, vy, sly, y.scale, num_splits=5, workspace=ws)
+    got = das.das_decode_attention(qx, kx, vx, slx, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], want_o) and torch.equal(got[1], want_l), "after another plan"
+    counters = ws[:cb].view(torch.int32)
+    assert int(torch.count_nonzero(counters)) == 0
