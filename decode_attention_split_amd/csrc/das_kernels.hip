@@ -61,8 +61,6 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
   return r;
 }
 
-__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
-
 __device__ __forceinline__ float lane_value(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
@@ -89,6 +87,31 @@ __device__ __forceinline__ float row_reduce16(float x) {
   x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
   return x;
 }
+
+// Sum (or max) of x over the lanes that differ from this one only in lane
+// bits kLoBit..5, in every one of them.  Bits 5 and 4 use the gfx950 row-swap
+// instructions (with both operands equal, the two results of a swap hold
+// x[i] and x[i^32], or x[i^16], between them); bit 3 uses a DPP row rotate
+// by 8 (lane i^8 within a 16-lane row).  No LDS traffic.
+template <int kLoBit, bool kMax>
+__device__ __forceinline__ float reduce_lane_bits(float x) {
+  static_assert(kLoBit >= 3 && kLoBit <= 6, "lane bits 3..5");
+  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  if constexpr (kLoBit <= 5) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (kLoBit <= 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (kLoBit <= 3) x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+constexpr int log2_int(int v) { return v <= 1 ? 0 : 1 + log2_int(v / 2); }
 
 // Raw buffer descriptor over `bytes` bytes at `base`: loads past the end
 // return zeros, so a split's rows past its end need no branch.
@@ -174,9 +197,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 // reused at the end for the wave merge.
 template <int D, int G>
 constexpr int split_smem_bytes() {
-  constexpr int kWaveBytes = kTile * 2 * D + kTile * G * 4;
-  constexpr int kMergeBytes = (G * D + 2 * G) * 4;
-  return kWaves * (kWaveBytes > kMergeBytes ? kWaveBytes : kMergeBytes);
+  return kWaves * (kTile * 2 * D + kTile * G * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,13 +213,16 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   constexpr int kKTileBytes = kTile * kRowBytes;
   constexpr int kPBytes = kTile * G * 4;
   constexpr int kWaveBytes = kKTileBytes + kPBytes;
-  constexpr int kMergeBytes = (G * D + 2 * G) * 4;
   constexpr int kSmemBytes = split_smem_bytes<D, G>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
   static_assert(kKTileBytes == kLoads * 1024, "one 1 KiB LDS slab per K load");
-  static_assert((kThreads > G * D / 4 ? kThreads : G * D / 4) * 16 + kThreads * 4 +
-                        kWaves * G * 4 <= kSmemBytes,
-                "fused merge scratch must fit in the tile LDS");
+  static_assert(kSmemBytes == kWaves * kWaveBytes, "one tile region per wave");
+  // End-of-stream state of a wave: its p.V sums are kept per row group
+  // (lanes with the same row of a load) rather than summed across the wave,
+  // as many row groups as fit in the wave's own tile region.
+  constexpr int kRowGroups = 64 / kLanesPerRow;                     // 4 (D=128) or 8 (D=64)
+  constexpr int kKeptGroups = kRowGroups < 16 / G ? kRowGroups : 16 / G;
+  static_assert(kKeptGroups * G * D * 4 <= kWaveBytes, "wave state fits in its tile region");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
@@ -391,8 +415,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       const bool ok = r0 + n < row_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int off = kTile; off < 64; off <<= 1) x[h] += xor_shfl(x[h], off);
+        x[h] = reduce_lane_bits<log2_int(kTile), false>(x[h]);  // add the parts of D
         x[h] = ok ? x[h] * c2 : -INFINITY;
         const float mt = row_reduce16<true>(x[h]);
         float tile_max = lane_value(mt, 0);
@@ -461,14 +484,17 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     }
   }
 
-  // ---- wave totals ----
-  // acc: sum the lanes that share a chunk of D (the rows of one load)
-#pragma unroll
-  for (int off = kLanesPerRow; off < 64; off <<= 1)
+  // ---- end of the stream: each wave's state into its own tile region ----
+  // acc: lanes lane and lane ^ 2^k for the row-group bits above kKeptGroups
+  // are summed (none for D = 128 with G <= 4); the lanes whose top bits are
+  // zero then hold row group rg = lane / kLanesPerRow.
+  constexpr int kKeepBit = log2_int(kKeptGroups * kLanesPerRow);   // lowest lane bit summed
+  if constexpr (kKeepBit < 6) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += xor_shfl(acc[h][e], off);
+      for (int e = 0; e < 8; ++e) acc[h][e] = reduce_lane_bits<kKeepBit, false>(acc[h][e]);
+  }
   float l_tot[G];
   if constexpr (G >= 4) {
 #pragma unroll
@@ -484,32 +510,43 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       l_tot[h] = lane_value(t, 0) + (kTile == 32 ? lane_value(t, 16) : 0.f);
     }
   }
-
-  // ---- merge the waves through LDS ----
-  __syncthreads();  // every wave is done with its K tile and p buffer
-  float* mg = reinterpret_cast<float*>(smem + wave * kMergeBytes);
-  if (lane < kLanesPerRow) {
+  // The wave's K tile and p buffer are no longer needed, and no other wave
+  // touches them: the state goes there without waiting for the others.
+  // Layout [row group][head][D] floats; max and sum per head in wst_ml.
+  __shared__ float wst_ml[kWaves * 2 * G];
+  {
+    float* wst = reinterpret_cast<float*>(kt);
+    if (lane < kKeptGroups * kLanesPerRow) {
+      const int rg = lane / kLanesPerRow;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(mg + h * D + 8 * lane) =
-          make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(mg + h * D + 8 * lane + 4) =
-          make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      for (int h = 0; h < G; ++h) {
+        float* dst = wst + (rg * G + h) * D + 8 * chunk;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      }
     }
-  }
-  if (lane == 0) {
+    if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mg[G * D + h] = m_run[h];
-      mg[G * D + G + h] = l_tot[h];
+      for (int h = 0; h < G; ++h) {
+        wst_ml[wave * 2 * G + h] = m_run[h];
+        wst_ml[wave * 2 * G + G + h] = l_tot[h];
+      }
     }
   }
   __syncthreads();
 
+  // ---- merge the waves: one thread per (row group, head, float4 quad) ----
+  // lane = rg * kPairLanes + x, pair (head, quad) = wave * kPairLanes + x, so
+  // the row groups of a pair are lanes of one wave and add up with swaps.
   // A sequence that uses at most one split is finished by split 0's
   // workgroup; so is every sequence of a single-split plan.
   const bool finish_here = a.direct || (a.fused && nsb <= 1);
   constexpr int kQuads = D / 4;                 // float4 quads per output row
+  constexpr int kPairs = G * kQuads;
+  constexpr int kPairLanes = 64 / kKeptGroups;
+  constexpr int kMergeWaves = kPairs / kPairLanes;
+  static_assert(kPairs % kPairLanes == 0 && kMergeWaves <= kWaves, "whole waves merge");
   // Partials of this (b, kv-head): rows (head, split) of D floats, and
   // (max, sum) pairs.  Offsets stay far below 4 GiB within one kv-head.
   const size_t qh0 = (size_t)b * a.Hq + (size_t)g * G;   // first query head of the group
@@ -517,18 +554,20 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       make_rsrc(a.ws_o + (a.direct ? 0 : qh0 * a.ns * D), G * a.ns * D * 4);
   const __amdgpu_buffer_rsrc_t rml =
       make_rsrc(a.ws_ml + (a.direct ? 0 : qh0 * a.ns * 2), G * a.ns * 2 * 4);
-  for (int idx = tid; idx < G * kQuads; idx += kThreads) {
-    const int h = idx / kQuads, quad = idx % kQuads;
+  if (wave < kMergeWaves) {
+    const int rg = lane / kPairLanes, x = lane % kPairLanes;
+    const int pair = wave * kPairLanes + x;
+    const int h = pair / kQuads, quad = pair % kQuads;
     // every wave's state is read before any of it is used, so the LDS
     // reads overlap instead of taking one round trip per wave
     float mw[kWaves], lw[kWaves];
     float4 uw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float* mgw = reinterpret_cast<const float*>(smem + w * kMergeBytes);
-      mw[w] = mgw[G * D + h];
-      lw[w] = mgw[G * D + G + h];
-      uw[w] = *reinterpret_cast<const float4*>(mgw + h * D + 4 * quad);
+      mw[w] = wst_ml[w * 2 * G + h];
+      lw[w] = wst_ml[w * 2 * G + G + h];
+      uw[w] = *reinterpret_cast<const float4*>(
+          reinterpret_cast<const float*>(smem + w * kWaveBytes) + (rg * G + h) * D + 4 * quad);
     }
     float M = -INFINITY;
 #pragma unroll
@@ -545,17 +584,27 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       o.w = fmaf(f, uw[w].w, o.w);
       lsum = fmaf(f, lw[w], lsum);
     }
-    const size_t qh = qh0 + h;
-    if (finish_here) {
-      const float inv = (M == -INFINITY) ? 0.f : 1.f / lsum;
-      store_out4(a, qh * D + 4 * quad, o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-      if (quad == 0 && a.lse != nullptr)
-        a.lse[qh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(lsum)) * kLn2;
-    } else {
-      // device-coherent stores (sc1): the merging workgroup may run on another XCD
-      const int row = h * a.ns + s;
-      coherent_store16(ro, (row * D + 4 * quad) * 4, o);
-      if (quad == 0) coherent_store8(rml, row * 8, M, lsum);
+    // add the row groups (M and lsum are the same in all of them)
+    constexpr int kGroupBit = log2_int(kPairLanes);
+    if constexpr (kGroupBit < 6) {
+      o.x = reduce_lane_bits<kGroupBit, false>(o.x);
+      o.y = reduce_lane_bits<kGroupBit, false>(o.y);
+      o.z = reduce_lane_bits<kGroupBit, false>(o.z);
+      o.w = reduce_lane_bits<kGroupBit, false>(o.w);
+    }
+    if (rg == 0) {
+      const size_t qh = qh0 + h;
+      if (finish_here) {
+        const float inv = (M == -INFINITY) ? 0.f : 1.f / lsum;
+        store_out4(a, qh * D + 4 * quad, o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        if (quad == 0 && a.lse != nullptr)
+          a.lse[qh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+      } else {
+        // device-coherent stores (sc1): the merging workgroup may run on another XCD
+        const int row = h * a.ns + s;
+        coherent_store16(ro, (row * D + 4 * quad) * 4, o);
+        if (quad == 0) coherent_store8(rml, row * 8, M, lsum);
+      }
     }
   }
   if (!a.fused || finish_here) return;
@@ -579,89 +628,77 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   __syncthreads();
   if (!s_last) return;
 
-  // thread -> (head, float4 quad of D) pair and a subset of the splits
-  constexpr int kPairs = G * kQuads;
-  constexpr int kGroups = kPairs >= kThreads ? 1 : kThreads / kPairs;
-  constexpr int kPerRound = kThreads / kGroups;
-  float4* red4 = reinterpret_cast<float4*>(smem);                        // [kGroups][kPairs]
-  float* redl = reinterpret_cast<float*>(smem + kGroups * kPairs * 16);  // [kGroups][G]
-  float* redm = redl + kGroups * G;                                      // [kGroups][G]
-  __syncthreads();  // the wave-merge reads of the LDS are done
-
-  for (int pair0 = 0; pair0 < kPairs; pair0 += kPerRound) {
-    const int pair = pair0 + tid % kPerRound;
-    const int grp = tid / kPerRound;
-    const bool active = pair < kPairs;
-    const int h = active ? pair / kQuads : 0, quad = active ? pair % kQuads : 0;
+  // One thread per (split group, head, float4 quad): lane = grp * kGroupLanes
+  // + x, pair = wave * kGroupLanes + x.  Group grp takes splits grp,
+  // grp + kGroups, ...; the groups of a pair are lanes of one wave, so they
+  // combine with swaps, in a fixed order whichever workgroup merges.
+  constexpr int kGroups = kThreads / kPairs < 4 ? kThreads / kPairs : 4;
+  constexpr int kGroupLanes = 64 / kGroups;
+  constexpr int kFinalWaves = kPairs / kGroupLanes;
+  static_assert(kGroups >= 1 && kPairs % kGroupLanes == 0 && kFinalWaves <= kWaves,
+                "whole waves merge the splits");
+  if (wave >= kFinalWaves) return;
+  const int grp = lane / kGroupLanes, x = lane % kGroupLanes;
+  const int pair = wave * kGroupLanes + x;
+  const int h = pair / kQuads, quad = pair % kQuads;
+  // This thread's splits, merged online: batches of 8 loaded in one round
+  // trip, the running sums rescaled when a batch raises the running max.
+  float mt = -INFINITY;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = 0.f;
+  constexpr int kBatch = 8;
+  for (int c0 = grp; c0 < nsb; c0 += kBatch * kGroups) {
+    float2 st[kBatch];
+    float4 u[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + k * kGroups;
+      if (c < nsb) {
+        st[k] = coherent_load8(rml, (h * a.ns + c) * 8);
+        u[k] = coherent_load16(ro, ((h * a.ns + c) * D + 4 * quad) * 4);
+      } else {
+        st[k] = make_float2(-INFINITY, 0.f);
+        u[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float bm = st[0].x;
+#pragma unroll
+    for (int k = 1; k < kBatch; ++k) bm = fmaxf(bm, st[k].x);
+    const float mn = fmaxf(mt, bm);  // finite: split c0 < nsb is in the batch
+    const float alpha = fast_exp2(mt - mn);
+    o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
+    ls *= alpha;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = fast_exp2(st[k].x - mn);  // 0 for the padding slots
+      o.x = fmaf(w, u[k].x, o.x);
+      o.y = fmaf(w, u[k].y, o.y);
+      o.z = fmaf(w, u[k].z, o.z);
+      o.w = fmaf(w, u[k].w, o.w);
+      ls = fmaf(w, st[k].y, ls);
+    }
+    mt = mn;
+  }
+  // combine the groups: global max, rescale, sum (a group without splits
+  // has max -inf and weighs 0)
+  constexpr int kGroupBit = log2_int(kGroupLanes);
+  float M = mt;
+  if constexpr (kGroupBit < 6) M = reduce_lane_bits<kGroupBit, true>(mt);
+  const float f = (mt == -INFINITY) ? 0.f : fast_exp2(mt - M);
+  o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+  ls *= f;
+  if constexpr (kGroupBit < 6) {
+    o.x = reduce_lane_bits<kGroupBit, false>(o.x);
+    o.y = reduce_lane_bits<kGroupBit, false>(o.y);
+    o.z = reduce_lane_bits<kGroupBit, false>(o.z);
+    o.w = reduce_lane_bits<kGroupBit, false>(o.w);
+    ls = reduce_lane_bits<kGroupBit, false>(ls);
+  }
+  if (grp == 0) {
     const size_t qh = qh0 + h;
-    // This thread's splits, merged online: batches of 8 loaded in one round
-    // trip, the running sums rescaled when a batch raises the running max.
-    float mt = -INFINITY;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float ls = 0.f;
-    if (active) {
-      constexpr int kBatch = 8;
-      for (int c0 = grp; c0 < nsb; c0 += kBatch * kGroups) {
-        float2 st[kBatch];
-        float4 u[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const int c = c0 + k * kGroups;
-          if (c < nsb) {
-            st[k] = coherent_load8(rml, (h * a.ns + c) * 8);
-            u[k] = coherent_load16(ro, ((h * a.ns + c) * D + 4 * quad) * 4);
-          } else {
-            st[k] = make_float2(-INFINITY, 0.f);
-            u[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-        float bm = st[0].x;
-#pragma unroll
-        for (int k = 1; k < kBatch; ++k) bm = fmaxf(bm, st[k].x);
-        const float mn = fmaxf(mt, bm);  // finite: split c0 < nsb is in the batch
-        const float alpha = fast_exp2(mt - mn);
-        o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
-        ls *= alpha;
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-          const float w = fast_exp2(st[k].x - mn);  // 0 for the padding slots
-          o.x = fmaf(w, u[k].x, o.x);
-          o.y = fmaf(w, u[k].y, o.y);
-          o.z = fmaf(w, u[k].z, o.z);
-          o.w = fmaf(w, u[k].w, o.w);
-          ls = fmaf(w, st[k].y, ls);
-        }
-        mt = mn;
-      }
-    }
-    if (active) {
-      red4[grp * kPairs + pair] = o;
-      if (quad == 0) {
-        redl[grp * G + h] = ls;
-        redm[grp * G + h] = mt;
-      }
-    }
-    __syncthreads();
-    if (active && grp == 0) {
-      float M = redm[h];
-      for (int gi = 1; gi < kGroups; ++gi) M = fmaxf(M, redm[gi * G + h]);
-      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-      float lt = 0.f;
-      for (int gi = 0; gi < kGroups; ++gi) {
-        const float mg = redm[gi * G + h];
-        const float f = (mg == -INFINITY) ? 0.f : fast_exp2(mg - M);
-        const float4 u = red4[gi * kPairs + pair];
-        t.x = fmaf(f, u.x, t.x);
-        t.y = fmaf(f, u.y, t.y);
-        t.z = fmaf(f, u.z, t.z);
-        t.w = fmaf(f, u.w, t.w);
-        lt = fmaf(f, redl[gi * G + h], lt);
-      }
-      const float inv = 1.f / lt;
-      store_out4(a, qh * D + 4 * quad, t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-      if (quad == 0 && a.lse != nullptr) a.lse[qh] = (M + __log2f(lt)) * kLn2;
-    }
-    __syncthreads();  // before the next round reuses the LDS
+    const float inv = 1.f / ls;
+    store_out4(a, qh * D + 4 * quad, o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (quad == 0 && a.lse != nullptr) a.lse[qh] = (M + __log2f(ls)) * kLn2;
   }
 }
 
@@ -834,7 +871,7 @@ static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipSt
   // half a CU's LDS, so no second workgroup fits on the CU; a grid with no
   // more workgroups than CUs then spreads over all of them instead of
   // doubling up on some.  The static part already counts toward the total.
-  constexpr int kStatic = split_smem_bytes<D, G>() + 64;  // + small scalars
+  constexpr int kStatic = split_smem_bytes<D, G>() + kWaves * 2 * G * 4 + 64;  // + wave maxima/sums, scalars
   static_assert(kStatic + 0 <= kMaxLdsPerWorkgroup, "static LDS over the limit");
   constexpr int kPad = kStatic < kOnePerCuLds ? kOnePerCuLds - kStatic : 0;
   static_assert(kStatic + kPad <= kMaxLdsPerWorkgroup, "padded LDS over the limit");
