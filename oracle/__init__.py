@@ -16,6 +16,10 @@ Pieces:
   same post (per-chunk max/sum/unnormalised output, then global max,
   correction factors, global sum, division).  Used only to pin that the
   split is exact.
+* ``attention_fp8`` / ``e4m3_decode`` -- the same definition over an 8-bit
+  floating-point K/V cache (FlashDecoding++ post, §4: quantised K/V turned
+  back into wider floats inside the kernel), read as OCP E4M3 codes with one
+  fp32 scale per kv-head for K and one for V.
 * ``merge`` -- the LSE / online-softmax merge of two attention states that
   the SGLang Diffusion "Parallelism Overview" page relies on for ring hops and
   tail parts ("What happens to the shapes", "Constraints").
@@ -90,6 +94,11 @@ class OracleLib:
         lib.das_oracle_split_attention.restype = None
         lib.das_oracle_merge.argtypes = [p, p, p, p, ctypes.c_int64, i32, p, p]
         lib.das_oracle_merge.restype = None
+        lib.das_oracle_e4m3_decode.argtypes = [p, ctypes.c_int64, p]
+        lib.das_oracle_e4m3_decode.restype = None
+        lib.das_oracle_attention_fp8.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                                 ctypes.c_double, p, p]
+        lib.das_oracle_attention_fp8.restype = None
         lib.das_oracle_max_threads.argtypes = []
         lib.das_oracle_max_threads.restype = ctypes.c_int
         lib.das_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -129,6 +138,38 @@ class OracleLib:
                                             _ptr(lse))
         return out, lse
 
+    def e4m3_decode(self, codes) -> np.ndarray:
+        """Values of OCP E4M3 codes (uint8), as float64; NaN for the NaN codes."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape, dtype=np.float64)
+        self.lib.das_oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out))
+        return out
+
+    def attention_fp8(self, q, k, v, k_scale, v_scale, seq_lens,
+                      scale: float) -> Tuple[np.ndarray, np.ndarray]:
+        """Unsplit fp64 attention over an E4M3 K/V cache: q bf16 bits (uint16),
+        k/v E4M3 codes (uint8), k_scale/v_scale fp32 per kv-head."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint8)
+        v = np.ascontiguousarray(v, dtype=np.uint8)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+        if q.ndim != 3 or k.ndim != 4 or k.shape != v.shape:
+            raise ValueError("q must be [B,Hq,D]; k and v [B,Hkv,Smax,D] of the same shape")
+        B, Hq, D = q.shape
+        Hkv, smax = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != D or Hq % Hkv or seq_lens.shape != (B,):
+            raise ValueError("inconsistent shapes")
+        if k_scale.shape != (Hkv,) or v_scale.shape != (Hkv,):
+            raise ValueError("k_scale and v_scale must be [Hkv]")
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        self.lib.das_oracle_attention_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(seq_lens), B, Hq, Hkv, smax, D, float(scale),
+                                          _ptr(out), _ptr(lse))
+        return out, lse
+
     def merge(self, o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
         """LSE merge of two states; o_* are [..., D], lse_* are [...]."""
         o_a = np.ascontiguousarray(o_a, dtype=np.float64)
@@ -166,6 +207,14 @@ def split_attention(q, k, v, seq_lens, scale: float, chunk: int):
 
 def merge(o_a, lse_a, o_b, lse_b):
     return default().merge(o_a, lse_a, o_b, lse_b)
+
+
+def e4m3_decode(codes):
+    return default().e4m3_decode(codes)
+
+
+def attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale: float):
+    return default().attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale)
 
 
 def max_threads() -> int:

@@ -230,3 +230,82 @@ void das_oracle_merge(const double* o_a, const double* lse_a, const double* o_b,
     lse_out[r] = lse;
   }
 }
+
+/*
+ * 8-bit floating point K/V cache ([FD++] §4: quantised K and V are read from
+ * memory and turned back into wider floats before the products).  The pages
+ * name FP8 but not its encoding or scaling; the readings taken here are
+ * OCP E4M3 codes and one fp32 scale per kv-head for K and one for V, so that
+ * the cached value of element d of row j of kv-head g is
+ * k_scale[g] * e4m3(code).
+ *
+ * E4M3 (OCP 8-bit floating point, "E4M3" encoding): sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits.  Exponent field 0 holds the subnormals
+ * m * 2^-9; exponent 1..15 the normals (1 + m/8) * 2^(e - 7), except that
+ * exponent 15 with mantissa 7 is NaN.  There are no infinities.
+ */
+static double e4m3_value(uint8_t code) {
+  const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+void das_oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+}
+
+/*
+ * Unsplit attention over an E4M3 K/V cache: the same definition as
+ * das_oracle_attention with k = k_scale[g] * e4m3(code), v likewise (the
+ * product is exact in double: 4 + 24 significant bits).
+ * k, v: [B][Hkv][Smax][D] codes; k_scale, v_scale: [Hkv] fp32.
+ */
+void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / G;
+      const int L = clamp_len(seq_lens[b], Smax);
+      const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
+      const uint8_t* kbase = k + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      const uint8_t* vbase = v + ((size_t)b * Hkv + g) * (size_t)Smax * D;
+      const double ks = (double)k_scale[g], vs = (double)v_scale[g];
+      double* o = out + ((size_t)b * Hq + h) * D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (L == 0) {
+        lse[(size_t)b * Hq + h] = -INFINITY;
+        continue;
+      }
+      double* w = (double*)malloc(sizeof(double) * (size_t)L);
+      double M = -INFINITY;
+      for (int j = 0; j < L; ++j) {
+        const uint8_t* krow = kbase + (size_t)j * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += widen_bf16(qrow[d]) * (ks * e4m3_value(krow[d]));
+        w[j] = scale * dot;
+        if (w[j] > M) M = w[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j < L; ++j) {
+        w[j] = exp(w[j] - M);
+        Z += w[j];
+      }
+      for (int j = 0; j < L; ++j) {
+        const uint8_t* vrow = vbase + (size_t)j * D;
+        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * e4m3_value(vrow[d]));
+      }
+      for (int d = 0; d < D; ++d) o[d] /= Z;
+      lse[(size_t)b * Hq + h] = M + log(Z);
+      free(w);
+    }
+  }
+}

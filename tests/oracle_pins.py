@@ -320,6 +320,96 @@ def pin_merge_of_halves_equals_whole(lib):
 
 
 # cheap pins first, the page-sized equivalence check last
+# ---- 8-bit (E4M3) K/V cache: FlashDecoding++ post §4 ----
+
+def _small_fp8(seed, B=2, Hq=4, Hkv=2, D=16, smax=24, lens=(24, 13), k_mult=1.0):
+    cfg = workloads.custom_config(B, Hq, Hkv, D, smax, k_mult=k_mult)
+    return workloads.make_fp8_inputs(cfg, seed, smax=smax, seq_lens=lens)
+
+
+def pin_e4m3_decode_matches_torch(lib):
+    """All 256 codes decode as torch's own float8_e4m3fn does (an independent implementation)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    mine = lib.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref)), "NaN codes differ"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok]), "E4M3 values differ from torch"
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok])), "signs of zero differ"
+
+
+def pin_e4m3_special_values(lib):
+    """Values the E4M3 format fixes: zeros, smallest subnormal and normal, one,
+    the largest finite value 448, the NaN codes, and ordering of the codes."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xFE: -448.0,
+             0xB8: -1.0}
+    codes = np.array(sorted(table), dtype=np.uint8)
+    got = lib.e4m3_decode(codes)
+    for c, g in zip(codes, got):
+        assert g == table[int(c)], f"code 0x{int(c):02X} -> {g}, want {table[int(c)]}"
+    all_vals = lib.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.isnan(all_vals[0x7F]) and np.isnan(all_vals[0xFF]), "0x7F / 0xFF must be NaN"
+    assert int(np.isnan(all_vals).sum()) == 2, "exactly two NaN codes, no infinities"
+    assert all_vals[0x80] == 0.0 and np.signbit(all_vals[0x80]), "0x80 is -0"
+    pos = all_vals[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes must increase"
+    assert np.array_equal(all_vals[0x80:0xFF], -pos), "sign bit negates"
+
+
+def pin_fp8_attention_equals_bf16_definition(lib):
+    """With these scales every k_scale*e4m3(code) is exact in bfloat16, so the
+    8-bit path must agree bitwise with the (pinned) bf16 definition fed the
+    dequantised values."""
+    x = _small_fp8(21, Hq=8, Hkv=2, D=32, smax=40, lens=(40, 17))
+    for mult in (1.0, 4.0):
+        if mult != 1.0:
+            x = _small_fp8(22, Hq=8, Hkv=2, D=32, smax=40, lens=(40, 17), k_mult=mult)
+        kd = lib.e4m3_decode(x.k) * x.k_scale[None, :, None, None].astype(np.float64)
+        vd = lib.e4m3_decode(x.v) * x.v_scale[None, :, None, None].astype(np.float64)
+        kb, vb = _bits(np.nan_to_num(kd)), _bits(np.nan_to_num(vd))
+        assert np.array_equal(_f(kb), np.nan_to_num(kd)) and np.array_equal(_f(vb), np.nan_to_num(vd)), \
+            "dequantised values must be exact in bf16 for this pin"
+        o8, l8 = lib.attention_fp8(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale)
+        ob, lb = lib.attention(x.q, kb, vb, x.seq_lens, x.scale)
+        assert np.array_equal(o8, ob) and np.array_equal(l8, lb), f"fp8 vs bf16 definition (k x{mult})"
+
+
+def pin_fp8_scale_folding(lib):
+    """Doubling k_scale is doubling the softmax scale; doubling v_scale doubles
+    the output and leaves the LSE alone (all exact scalings by 2)."""
+    x = _small_fp8(23)
+    o, l = lib.attention_fp8(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale)
+    o2, l2 = lib.attention_fp8(x.q, x.k, x.v, x.k_scale * 2, x.v_scale, x.seq_lens, x.scale)
+    o3, l3 = lib.attention_fp8(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale * 2)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3), "k_scale and scale must fold"
+    o4, l4 = lib.attention_fp8(x.q, x.k, x.v, x.k_scale, x.v_scale * 2, x.seq_lens, x.scale)
+    assert np.array_equal(o4, 2 * o) and np.array_equal(l4, l), "v_scale must scale the output only"
+    assert not np.allclose(o2, o), "k_scale must matter"
+
+
+def pin_fp8_bruteforce_tiny(lib):
+    """Non-dyadic per-head scales against a pure-Python textbook softmax with
+    math.fsum, the codes decoded by torch."""
+    import torch
+
+    x = _small_fp8(24, B=1, Hq=4, Hkv=2, D=8, smax=6, lens=(6,))
+    ks = np.array([0.1, 0.3], dtype=np.float32)
+    vs = np.array([0.7, 0.05], dtype=np.float32)
+    o, l = lib.attention_fp8(x.q, x.k, x.v, ks, vs, x.seq_lens, x.scale)
+    dec = lambda c: torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+    kf, vf, qf = dec(x.k), dec(x.v), _f(x.q)
+    for h in range(4):
+        g = h // 2
+        k_rows = [[float(ks[g]) * kf[0, g, j, d] for d in range(8)] for j in range(6)]
+        v_rows = [[float(vs[g]) * vf[0, g, j, d] for d in range(8)] for j in range(6)]
+        ro, rl = oracle.attention_fsum_textbook(list(qf[0, h]), k_rows, v_rows, x.scale)
+        assert np.allclose(o[0, h], ro, rtol=1e-12, atol=1e-14), f"head {h}"
+        assert abs(l[0, h] - rl) <= 1e-12 * max(1.0, abs(rl)), f"lse head {h}"
+
+
 ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_") and callable(v)),
                   key=lambda f: (f is pin_fd_equivalence_check, f.__name__))
 

@@ -23,6 +23,15 @@ Recipe (one config = one seed, ``seed = 42 + config index``):
   (0x7FC0) so that any kernel reading them contaminates its result.
 * ``scale = 1/sqrt(D)`` rounded to float32 (the library takes a float).
 
+8-bit (E4M3) K/V caches (``make_fp8_inputs``): q as above; per kv-head
+scales ``k_scale[g] = k_mult * (4 + g) / 64`` and ``v_scale[g] = (3 + g) / 64``
+(float32); the codes of K (``t = 2``) and V (``t = 3``) of batch row ``b``,
+kv-head ``h`` come from stream ``PCG64(seed).jumped(1 + (t*B + b)*Hkv + h)``:
+one float32 ``standard_normal`` draw over the valid rows, times ``k_mult``
+for K, divided by the head's scale, clamped to +-448 and rounded to the
+nearest E4M3 code (ties to even; torch's float8_e4m3fn conversion).  Rows past
+``seq_lens[b]`` hold the E4M3 NaN code 0x7F.
+
 The five named configs are the decode shapes the FlashDecoding++ post
 (techknowgenie, "FlashDecoding++: 시퀀스 차원 KV 분할 병렬화 ...") argues
 about in §1-§2: single-query decode, GQA with 8 KV heads, long context, a
@@ -186,3 +195,90 @@ def config_inputs(index: int) -> Inputs:
 def custom_config(B: int, Hq: int, Hkv: int, D: int, smax: int, name: str = "custom",
                   k_mult: float = 1.0) -> Config:
     return Config(name, B=B, Hq=Hq, Hkv=Hkv, D=D, smax=smax, k_mult=k_mult)
+
+
+E4M3_NAN = np.uint8(0x7F)
+
+
+def fp8_scales(cfg: Config):
+    """Per kv-head float32 scales (k_scale, v_scale) of the 8-bit caches."""
+    g = np.arange(cfg.Hkv, dtype=np.float64)
+    k_scale = (cfg.k_mult * (4.0 + g) / 64.0).astype(np.float32)
+    v_scale = ((3.0 + g) / 64.0).astype(np.float32)
+    return k_scale, v_scale
+
+
+def _fill_fp8_rows(seed: int, tensor: int, B: int, H: int, smax: int, D: int,
+                   lens: np.ndarray, head_scale: np.ndarray, mult: float = 1.0) -> np.ndarray:
+    """E4M3 codes of K (tensor 2) or V (tensor 3), NaN code beyond the valid rows."""
+    import torch
+
+    out = np.full((B, H, smax, D), E4M3_NAN, dtype=np.uint8)
+
+    def one(task: int) -> None:
+        b, h = divmod(task, H)
+        L = int(lens[b])
+        if L == 0:
+            return
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(1 + (tensor * B + b) * H + h))
+        x = rng.standard_normal(L * D, dtype=np.float32)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        x /= head_scale[h]
+        np.clip(x, -448.0, 448.0, out=x)
+        codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out[b, h, :L, :] = codes.reshape(L, D)
+
+    tasks = range(B * H)
+    workers = min(B * H, max(1, os.cpu_count() or 1), 16)
+    if workers <= 1 or B * H * int(lens.max(initial=0)) * D < (1 << 22):
+        for t in tasks:
+            one(t)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, tasks))
+    return out
+
+
+@dataclasses.dataclass
+class Fp8Inputs:
+    config: Config
+    seed: int
+    q: np.ndarray          # uint16 [B, Hq, D] bf16 bits
+    k: np.ndarray          # uint8 [B, Hkv, Smax, D] E4M3 codes
+    v: np.ndarray          # uint8 [B, Hkv, Smax, D] E4M3 codes
+    k_scale: np.ndarray    # float32 [Hkv]
+    v_scale: np.ndarray    # float32 [Hkv]
+    seq_lens: np.ndarray   # int32 [B]
+    scale: float
+
+    @property
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes: every valid row of K and V read once (1 byte per element)."""
+        c = self.config
+        return int(self.seq_lens.astype(np.int64).sum()) * c.Hkv * c.D * 2
+
+
+def make_fp8_inputs(cfg: Config, seed: int, smax: Optional[int] = None,
+                    seq_lens: Optional[Sequence[int]] = None) -> Fp8Inputs:
+    """One seeded input set for ``cfg`` with an 8-bit (E4M3) K/V cache."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    else:
+        lens = draw_seq_lens(cfg, rng)
+    B = len(lens)
+    S = int(smax if smax is not None else max(cfg.smax, int(lens.max(initial=0))))
+    if lens.size and (lens.min() < 0 or lens.max() > S):
+        raise ValueError("seq_lens must lie in [0, Smax]")
+    q = f32_to_bf16_bits(rng.standard_normal(B * cfg.Hq * cfg.D, dtype=np.float32))
+    q = q.reshape(B, cfg.Hq, cfg.D)
+    k_scale, v_scale = fp8_scales(cfg)
+    k = _fill_fp8_rows(seed, 2, B, cfg.Hkv, S, cfg.D, lens, k_scale, cfg.k_mult)
+    v = _fill_fp8_rows(seed, 3, B, cfg.Hkv, S, cfg.D, lens, v_scale)
+    return Fp8Inputs(cfg, seed, q, k, v, k_scale, v_scale, lens, cfg.scale)
+
+
+def config_fp8_inputs(index: int) -> Fp8Inputs:
+    """The named config ``index`` at its full size with an E4M3 cache, seed 42 + index."""
+    return make_fp8_inputs(CONFIGS[index], 42 + index)
