@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="index into workloads.CONFIGS")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="K/V cache element: bf16, or E4M3 codes with per-kv-head scales")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate; 0 = auto")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline; 0 skips it")
@@ -156,7 +158,8 @@ def main():
     das.load_library()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.config]
-    x = workloads.config_inputs(args.config)
+    fp8 = args.kv_dtype == "fp8"
+    x = workloads.config_fp8_inputs(args.config) if fp8 else workloads.config_inputs(args.config)
     B, Hq, D = x.q.shape
     Hkv, Smax = x.k.shape[1], x.k.shape[2]
     kv_bytes = x.kv_bytes
@@ -169,7 +172,11 @@ def main():
     sl = torch.from_numpy(x.seq_lens).to(dev)
     alloc = x.k.nbytes + x.v.nbytes
     copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
-    k0, v0 = up(x.k), up(x.v)
+    if fp8:
+        k0, v0 = torch.from_numpy(x.k).to(dev), torch.from_numpy(x.v).to(dev)
+        k_scale, v_scale = torch.from_numpy(x.k_scale).to(dev), torch.from_numpy(x.v_scale).to(dev)
+    else:
+        k0, v0 = up(x.k), up(x.v)
     ks, vs = [k0], [v0]
     for _ in range(copies - 1):
         ks.append(k0.clone())
@@ -183,8 +190,13 @@ def main():
     # One prepared decode-attention call per K/V copy.  It is a single kernel
     # launch: phase 1 plus the fused phase-2 merge by the last workgroup of
     # each (b, kv-head).
-    calls = [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
-                                args.splits, ws) for c in range(copies)]
+    if fp8:
+        calls = [das.prepare_decode("das_decode_attention_fp8", q, ks[c], vs[c], sl, x.scale, out,
+                                    lse, args.splits, ws, k_scale=k_scale, v_scale=v_scale)
+                 for c in range(copies)]
+    else:
+        calls = [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
+                                    args.splits, ws) for c in range(copies)]
 
     for i in range(args.warmup):
         calls[i % copies]()
@@ -218,7 +230,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 K/V, bf16 q" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
@@ -228,6 +240,7 @@ def main():
             "kv_bytes": kv_bytes,
             "num_splits": ns, "chunk": chunk,
             "out_dtype": args.out_dtype,
+            "kv_dtype": args.kv_dtype,
             "kv_copies_rotated": copies,
             "us_per_call": round(ms_per_step * 1e3, 2),
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -239,11 +252,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name, ns),
+            "traffic": None if fp8 else measured_traffic(cfg.name, ns),
             "kernel_us": round(kernel_ms * 1e3, 3),
         },
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not fp8:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -25,7 +25,8 @@ DAS_CHUNK_QUANTUM = 128
 DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 
 EXPORTED = ("das_plan", "das_decode_workspace_bytes", "das_decode_attention",
-            "das_split_kv_decode", "das_lse_combine", "das_merge_attn_states", "das_strerror")
+            "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
+            "das_lse_combine", "das_merge_attn_states", "das_strerror")
 
 _lib = None
 
@@ -54,6 +55,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     decode_args = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_float, p, i32, p, i32, p, sz, p]
     for name in ("das_decode_attention", "das_split_kv_decode"):
         getattr(lib, name).argtypes = decode_args
+        getattr(lib, name).restype = ctypes.c_int
+    fp8_args = [p, p, p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_float, p, i32, p, i32, p, sz, p]
+    for name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8"):
+        getattr(lib, name).argtypes = fp8_args
         getattr(lib, name).restype = ctypes.c_int
     lib.das_lse_combine.argtypes = [p, i32, i32, i32, i32, i32, i32, p, sz, p, i32, p, p]
     lib.das_lse_combine.restype = ctypes.c_int
@@ -100,14 +105,16 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _decode_shapes(q, k_cache, v_cache, seq_lens):
+def _decode_shapes(q, k_cache, v_cache, seq_lens, fp8: bool = False):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
-        raise ValueError("q, k_cache and v_cache must be bfloat16")
+    kv_dtypes = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
+    if q.dtype != torch.bfloat16 or k_cache.dtype not in kv_dtypes or v_cache.dtype not in kv_dtypes:
+        raise ValueError("q must be bfloat16; k_cache and v_cache bfloat16, or E4M3 codes "
+                         "(uint8 or float8_e4m3fn) for the fp8 entry points")
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -154,6 +161,26 @@ def _run_decode(fn_name, q, k_cache, v_cache, seq_lens, scale, out, lse_out, out
     return out, lse_out, workspace
 
 
+def _scales(k_scale, v_scale, Hkv):
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if not (t.is_cuda and t.is_contiguous()) or t.dtype != torch.float32 or t.shape != (Hkv,):
+            raise ValueError(f"{name} must be a contiguous float32 [Hkv] device tensor")
+
+
+def _run_decode_fp8(fn_name, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out,
+                    lse_out, out_dtype, num_splits, workspace, stream, with_lse):
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fp8=True)
+    _scales(k_scale, v_scale, Hkv)
+    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
+    dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    fn = getattr(load_library(), fn_name)
+    _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+              B, Hq, Hkv, Smax, D, float(scale), _ptr(out), dtype_code, _ptr(lse_out),
+              int(num_splits), _ptr(workspace), ws_bytes, _stream(stream)), fn_name)
+    return out, lse_out, workspace
+
+
 class PreparedCall:
     """One C-ABI call with its argument list marshalled once.
 
@@ -176,20 +203,27 @@ class PreparedCall:
 
 def prepare_decode(fn_name: str, q, k_cache, v_cache, seq_lens, scale: float,
                    out: torch.Tensor, lse_out: Optional[torch.Tensor], num_splits: int,
-                   workspace: torch.Tensor, stream=None) -> PreparedCall:
-    """Prepared das_decode_attention / das_split_kv_decode call (same checks once)."""
-    if fn_name not in ("das_decode_attention", "das_split_kv_decode"):
+                   workspace: torch.Tensor, stream=None, k_scale=None,
+                   v_scale=None) -> PreparedCall:
+    """Prepared das_decode_attention / das_split_kv_decode call, or their _fp8
+    forms (then with k_scale and v_scale); the same checks run once."""
+    fp8 = fn_name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8")
+    if not fp8 and fn_name not in ("das_decode_attention", "das_split_kv_decode"):
         raise ValueError(fn_name)
-    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fp8=fp8)
+    if fp8:
+        _scales(k_scale, v_scale, Hkv)
     out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out.dtype, lse_out is not None)
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, num_splits):
         raise DasError(DAS_EWORKSPACE, fn_name)
     code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
-    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, Smax, D,
-            ctypes.c_float(scale), _ptr(out), code, _ptr(lse_out), int(num_splits),
-            _ptr(workspace), ws_bytes, _stream(stream))
-    return PreparedCall(fn_name, args, (q, k_cache, v_cache, seq_lens, out, lse_out, workspace))
+    scales = (_ptr(k_scale), _ptr(v_scale)) if fp8 else ()
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache)) + scales + (
+        _ptr(seq_lens), B, Hq, Hkv, Smax, D, ctypes.c_float(scale), _ptr(out), code,
+        _ptr(lse_out), int(num_splits), _ptr(workspace), ws_bytes, _stream(stream))
+    return PreparedCall(fn_name, args, (q, k_cache, v_cache, seq_lens, out, lse_out, workspace,
+                                        k_scale, v_scale))
 
 
 def prepare_lse_combine(seq_lens, Hq: int, Hkv: int, Smax: int, D: int, workspace, out,
@@ -221,6 +255,26 @@ def das_split_kv_decode(q, k_cache, v_cache, seq_lens, scale, out=None, lse_out=
     """Phase 1 only; returns (out, lse, workspace).  Finish with das_lse_combine."""
     return _run_decode("das_split_kv_decode", q, k_cache, v_cache, seq_lens, scale, out, lse_out,
                        out_dtype, num_splits, workspace, stream, with_lse)
+
+
+def das_decode_attention_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out=None,
+                             lse_out=None, out_dtype=torch.float32, num_splits=0, workspace=None,
+                             stream=None, with_lse=True):
+    """Decode attention over an E4M3 K/V cache (codes as uint8 or float8_e4m3fn,
+    fp32 scales [Hkv] for K and V); returns (out, lse)."""
+    out, lse_out, _ = _run_decode_fp8("das_decode_attention_fp8", q, k_cache, v_cache, k_scale,
+                                      v_scale, seq_lens, scale, out, lse_out, out_dtype,
+                                      num_splits, workspace, stream, with_lse)
+    return out, lse_out
+
+
+def das_split_kv_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out=None,
+                            lse_out=None, out_dtype=torch.float32, num_splits=0, workspace=None,
+                            stream=None, with_lse=True):
+    """Phase 1 alone over an E4M3 K/V cache; returns (out, lse, workspace)."""
+    return _run_decode_fp8("das_split_kv_decode_fp8", q, k_cache, v_cache, k_scale, v_scale,
+                           seq_lens, scale, out, lse_out, out_dtype, num_splits, workspace,
+                           stream, with_lse)
 
 
 def das_lse_combine(seq_lens: torch.Tensor, Hq: int, Hkv: int, Smax: int, D: int,

@@ -122,10 +122,21 @@ struct Checked {
 };
 
 // Checks shared by every decode entry point.  Nothing is launched on failure.
+// The K/V cache of one call: bf16 rows, or E4M3 codes with fp32 scales per
+// kv-head (FlashDecoding++ post, §4).
+struct KvCache {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  bool fp8;
+  int elem_bytes() const { return fp8 ? 1 : 2; }
+};
+
 int check_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
                  int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, const void* out,
                  int32_t out_dtype, int32_t num_splits, const void* workspace,
-                 size_t workspace_bytes, bool need_inputs, Checked* c) {
+                 size_t workspace_bytes, bool need_inputs, int elem_bytes, Checked* c) {
   if (seq_lens == nullptr || out == nullptr) return DAS_EINVAL;
   if (need_inputs && (q == nullptr || k == nullptr || v == nullptr)) return DAS_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || D < 1) return DAS_EINVAL;
@@ -136,7 +147,7 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   if (!supported_dims(D, G)) return DAS_ENOTSUP;
   // a sequence's K (or V) rows, plus one tile of overhang, are addressed
   // with 32-bit byte offsets
-  if ((int64_t)(Smax + 256) * D * 2 > INT32_MAX) return DAS_ENOTSUP;
+  if ((int64_t)(Smax + 256) * D * elem_bytes > INT32_MAX) return DAS_ENOTSUP;
   if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
   if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
   int32_t ns = 0, chunk = 0;
@@ -152,16 +163,15 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   return DAS_OK;
 }
 
-// Rows per block a split streams: the whole chunk, or (interleaved plans)
-// one block of kWaves * kTile rows per step, split s taking blocks s, s+ns, ...
-int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
-               int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out,
-               int32_t out_dtype, float* lse_out, void* workspace, const Checked& c, bool fused,
-               hipStream_t st) {
+int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_t B, int32_t Hq,
+               int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+               float* lse_out, void* workspace, const Checked& c, bool fused, hipStream_t st) {
   das::SplitArgs a{};
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
+  a.k = kv.k;
+  a.v = kv.v;
+  a.k_scale = kv.k_scale;
+  a.v_scale = kv.v_scale;
   a.seq_lens = seq_lens;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -184,8 +194,9 @@ int run_phase1(const void* q, const void* k, const void* v, const int32_t* seq_l
   int cus = 0;
   if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
   const bool one_per_cu = DAS_ONE_PER_CU && (int64_t)B * Hkv * c.ns <= cus;
-  return das::launch_split_kv_decode(D, c.G, B, a, one_per_cu, st) == hipSuccess ? DAS_OK
-                                                                                 : DAS_ELAUNCH;
+  return das::launch_split_kv_decode(D, c.G, kv.fp8, B, a, one_per_cu, st) == hipSuccess
+             ? DAS_OK
+             : DAS_ELAUNCH;
 }
 
 int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int32_t D,
@@ -205,6 +216,44 @@ int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int
   a.lse = lse_out;
   a.out_bf16 = out_dtype == DAS_BF16;
   return das::launch_lse_combine(D, B, a, st) == hipSuccess ? DAS_OK : DAS_ELAUNCH;
+}
+
+int split_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_t B, int32_t Hq,
+               int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+               float* lse_out, int32_t num_splits, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  Checked c{};
+  const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
+                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c);
+  if (rc != DAS_OK) return rc;
+  return run_phase1(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                    workspace, c, false, static_cast<hipStream_t>(stream));
+}
+
+int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                int32_t Hkv, int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
+                float* lse_out, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  Checked c{};
+  const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
+                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c);
+  if (rc != DAS_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // One launch: the last workgroup of each (b, kv-head) merges the splits.
+  // Every split workgroup then ends with a store-completion wait and a
+  // counter round trip while it holds its CU; with many more workgroups than
+  // CUs that costs more than a second, small merge kernel (B=64 varlen
+  // decode, 2560 workgroups: 375 us fused, 363 us as two kernels), so the
+  // merge is fused only up to kFusedWgsPerCu workgroups per CU.  Shapes with
+  // more (b, kv-head) pairs than counter slots always use the second kernel.
+  int cus = 0;
+  if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
+  const bool fused = (int64_t)B * Hkv <= das::kCounterSlots &&
+                     (int64_t)B * Hkv * c.ns <= kFusedWgsPerCu * cus;
+  const int rc1 = run_phase1(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                             workspace, c, fused, st);
+  if (rc1 != DAS_OK || fused) return rc1;
+  return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c, st);
 }
 
 }  // namespace
@@ -231,12 +280,21 @@ int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
                         int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
                         float* lse_out, int32_t num_splits, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  Checked c{};
-  const int rc = check_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
-                              out_dtype, num_splits, workspace, workspace_bytes, true, &c);
-  if (rc != DAS_OK) return rc;
-  return run_phase1(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
-                    lse_out, workspace, c, false, static_cast<hipStream_t>(stream));
+  const KvCache kv{k_cache, v_cache, nullptr, nullptr, false};
+  return split_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                    num_splits, workspace, workspace_bytes, stream);
+}
+
+int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                            float scale, void* out, int32_t out_dtype, float* lse_out,
+                            int32_t num_splits, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, true};
+  return split_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                    num_splits, workspace, workspace_bytes, stream);
 }
 
 int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax,
@@ -245,7 +303,7 @@ int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                     void* stream) {
   Checked c{};
   const int rc = check_decode(nullptr, nullptr, nullptr, seq_lens, B, Hq, Hkv, Smax, D, 1.0f, out,
-                              out_dtype, num_splits, workspace, workspace_bytes, false, &c);
+                              out_dtype, num_splits, workspace, workspace_bytes, false, 1, &c);
   if (rc != DAS_OK) return rc;
   return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c,
                     static_cast<hipStream_t>(stream));
@@ -256,26 +314,21 @@ int das_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
                          float* lse_out, int32_t num_splits, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  Checked c{};
-  const int rc = check_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
-                              out_dtype, num_splits, workspace, workspace_bytes, true, &c);
-  if (rc != DAS_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  // One launch: the last workgroup of each (b, kv-head) merges the splits.
-  // Every split workgroup then ends with a store-completion wait and a
-  // counter round trip while it holds its CU; with many more workgroups than
-  // CUs that costs more than a second, small merge kernel (B=64 varlen
-  // decode, 2560 workgroups: 375 us fused, 363 us as two kernels), so the
-  // merge is fused only up to kFusedWgsPerCu workgroups per CU.  Shapes with
-  // more (b, kv-head) pairs than counter slots always use the second kernel.
-  int cus = 0;
-  if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
-  const bool fused = (int64_t)B * Hkv <= das::kCounterSlots &&
-                     (int64_t)B * Hkv * c.ns <= kFusedWgsPerCu * cus;
-  const int rc1 = run_phase1(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, Smax, D, scale, out,
-                             out_dtype, lse_out, workspace, c, fused, st);
-  if (rc1 != DAS_OK || fused) return rc1;
-  return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c, st);
+  const KvCache kv{k_cache, v_cache, nullptr, nullptr, false};
+  return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                     num_splits, workspace, workspace_bytes, stream);
+}
+
+int das_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                             float scale, void* out, int32_t out_dtype, float* lse_out,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, true};
+  return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                     num_splits, workspace, workspace_bytes, stream);
 }
 
 int das_merge_attn_states(const void* o_a, const float* lse_a, const void* o_b,

@@ -34,8 +34,10 @@ static_assert(kTile == 16 || kTile == 32, "tile must be 16 or 32 rows");
 // (split, kv-head, batch row); it holds every query head of that kv-head.
 struct SplitArgs {
   const uint16_t* q;         // bf16 [B][Hq][D]
-  const uint16_t* k;         // bf16 [B][Hkv][Smax][D]
-  const uint16_t* v;         // bf16 [B][Hkv][Smax][D]
+  const void* k;             // [B][Hkv][Smax][D] bf16, or E4M3 codes
+  const void* v;             // [B][Hkv][Smax][D] bf16, or E4M3 codes
+  const float* k_scale;      // E4M3 cache: fp32 [Hkv] (FlashDecoding++ post, §4); else unused
+  const float* v_scale;
   const int32_t* seq_lens;   // int32 [B]
   int32_t Hq, Hkv, Smax;
   int32_t chunk, ns;         // rows per split, splits
@@ -83,8 +85,8 @@ struct MergeArgs {
 // a second one on its CU.
 constexpr int kMaxLdsPerWorkgroup = 160 * 1024;
 constexpr int kOnePerCuLds = 84 * 1024;
-hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
-                                  hipStream_t stream);
+hipError_t launch_split_kv_decode(int D, int G, bool fp8, int B, const SplitArgs& a,
+                                  bool one_per_cu, hipStream_t stream);
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
 hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t stream);
 

@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "das_internal.h"
 
 namespace das {
@@ -125,15 +127,42 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Byte offset of the 16-byte chunk `c` of row `r` in a wave's K tile.  Rows
-// are 2*D bytes; chunk slots are XOR-swizzled with the row index so that the
-// 16 lanes that store one row, and the 16 lanes that read one chunk column
-// of 16 rows, each hit 16 distinct 16-byte bank groups.
-template <int D>
+// Byte offset of the 16-byte chunk `c` of row `r` in a wave's K tile of
+// kRowBytes-byte rows.  Chunk slots are XOR-swizzled with the row's 256-byte
+// LDS bank row, so that the lanes that store one row, and the lanes that read
+// one column of 16 rows, hit distinct bank groups.
+template <int kRowBytes>
 __device__ __forceinline__ int k_tile_offset(int r, int c) {
-  constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  constexpr int kRowsPerBank = 256 / (2 * D);  // rows per 256-byte LDS bank row
-  return r * (2 * D) + ((c ^ ((r / kRowsPerBank) % kChunks)) << 4);
+  constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+  constexpr int kRowsPerBank = 256 / kRowBytes;  // rows per 256-byte LDS bank row
+  return r * kRowBytes + ((c ^ ((r / kRowsPerBank) % kChunks)) << 4);
+}
+
+// Eight E4M3 codes (OCP 8-bit floating point) as eight bf16 values; the
+// conversion is exact (4 significant bits, a subset of bf16's range).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
+// Eight E4M3 codes as fp32, in order.
+__device__ __forceinline__ void e4m3x8_to_f32(uint2 w, float* f) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, DAS_KV_CACHE_POLICY);
+  return make_uint2(v[0], v[1]);
 }
 
 // Stores and loads with the sc1 cache policy: coherent at device scope, so a
@@ -193,36 +222,54 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Static LDS of split_kv_decode<D, G>: per wave a K tile and a p buffer,
-// reused at the end for the wave merge.
-template <int D, int G>
+// Static LDS of split_kv_decode<D, G, kFp8>: per wave a K tile and a p
+// buffer, reused at the end for the wave's state.
+template <int D, int G, bool kFp8>
 constexpr int split_smem_bytes() {
-  return kWaves * (kTile * 2 * D + kTile * G * 4);
+  return kWaves * (kTile * (kFp8 ? 1 : 2) * D + kTile * G * 4);
 }
+
+constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
 
 // ---------------------------------------------------------------------------
 // Phase 1: split_kv_decode.  Grid (ns | 1, Hkv, B), kThreads threads.
+// kFp8: K and V are E4M3 codes with one fp32 scale per kv-head each
+// (FlashDecoding++ post, §4), dequantised on chip; otherwise bf16.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool kFp8>
 __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     void split_kv_decode_kernel(SplitArgs a) {
-  constexpr int kLanesPerRow = D / 8;           // lanes covering one K/V row, 16 B each
+  constexpr int kElemBytes = kFp8 ? 1 : 2;
+  constexpr int kT = kTile;                     // rows per wave per step
+  constexpr int kRowBytes = D * kElemBytes;
+  // V: every lane loads 8 elements (16 bytes of bf16, 8 bytes of E4M3) of
+  // one row, D/8 consecutive lanes covering the row; the p.V sums use the
+  // same layout.
+  constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  constexpr int kLoads = kTile / kRowsPerLoad;  // 16-byte loads per lane per tile (K or V)
-  constexpr int kRowBytes = 2 * D;
-  constexpr int kKTileBytes = kTile * kRowBytes;
-  constexpr int kPBytes = kTile * G * 4;
+  constexpr int kLoads = kT / kRowsPerLoad;  // V loads per lane per tile
+  constexpr int kVLaneBytes = 8 * kElemBytes;
+  // K: 16-byte loads straight into LDS, kKLanesPerRow lanes per row.
+  constexpr int kKLanesPerRow = kRowBytes / 16;
+  constexpr int kKRowsPerLoad = 64 / kKLanesPerRow;
+  constexpr int kKLoads = kT / kKRowsPerLoad;
+  constexpr int kKTileBytes = kT * kRowBytes;
+  constexpr int kPBytes = kT * G * 4;
   constexpr int kWaveBytes = kKTileBytes + kPBytes;
-  constexpr int kSmemBytes = split_smem_bytes<D, G>();
+  constexpr int kSmemBytes = split_smem_bytes<D, G, kFp8>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
-  static_assert(kKTileBytes == kLoads * 1024, "one 1 KiB LDS slab per K load");
+  static_assert(kKTileBytes == kKLoads * 1024, "one 1 KiB LDS slab per K load");
   static_assert(kSmemBytes == kWaves * kWaveBytes, "one tile region per wave");
   // End-of-stream state of a wave: its p.V sums are kept per row group
   // (lanes with the same row of a load) rather than summed across the wave,
   // as many row groups as fit in the wave's own tile region.
   constexpr int kRowGroups = 64 / kLanesPerRow;                     // 4 (D=128) or 8 (D=64)
-  constexpr int kKeptGroups = kRowGroups < 16 / G ? kRowGroups : 16 / G;
-  static_assert(kKeptGroups * G * D * 4 <= kWaveBytes, "wave state fits in its tile region");
+  constexpr int kFitGroups = pow2_floor(kWaveBytes / (G * D * 4));
+  constexpr int kMergeGroups = kThreads * 4 / (G * D);   // one merging thread per group and quad
+  constexpr int kKeptGroups = kRowGroups < kFitGroups
+                                  ? (kRowGroups < kMergeGroups ? kRowGroups : kMergeGroups)
+                                  : (kFitGroups < kMergeGroups ? kFitGroups : kMergeGroups);
+  static_assert(kKeptGroups >= 1, "one wave state fits in its tile region");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
@@ -236,10 +283,9 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int L = clamp_len(a.seq_lens[b], a.Smax);
-  // The sequence's rows are cut into blocks of a.chunk rows; split s owns
-  // blocks s, s + ns, s + 2*ns, ...  (one block per split when the block is
-  // the whole chunk ceil(Smax/ns)).
-  const int nb = (L + a.chunk - 1) / a.chunk;   // blocks holding valid rows
+  // The sequence's rows are cut into chunks of a.chunk rows; split s owns
+  // chunk s (chunk * ns >= Smax, so every row has a split).
+  const int nb = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
   const int nsb = min(a.ns, nb);                // splits this sequence uses
   // An empty split exits at once; phase 2 never reads it.  With the fused
   // merge, split 0 of an empty sequence stays to write out = 0, lse = -inf.
@@ -250,21 +296,32 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   // The sequence's valid rows of K and V as bounds-checked buffers: loads
   // past row L return zeros, and the rows beyond seq_lens are never read.
-  const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax * D;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + slab, L * kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + slab, L * kRowBytes);
+  const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax * kRowBytes;  // bytes
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + slab, L * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + slab, L * kRowBytes);
   int row_end = 0;                              // end of the block being streamed
-  const int row_in_load = lane / kLanesPerRow;  // this lane's row within a load
-  const int chunk = lane % kLanesPerRow;        // this lane's 16-byte chunk of a row
-  const int lane_off = row_in_load * kRowBytes + 16 * chunk;
-  const float c2 = a.scale_log2e;
+  const int row_in_load = lane / kLanesPerRow;  // this lane's V row within a load
+  const int chunk = lane % kLanesPerRow;        // this lane's 8 elements of a V row
+  const int lane_off = row_in_load * kRowBytes + kVLaneBytes * chunk;
+  const int k_row_in_load = lane / kKLanesPerRow;
+  const int k_slot = lane % kKLanesPerRow;
+  // Logits in base-2 units; an E4M3 cache's K scale multiplies the finished
+  // dot product, its V scale the finished p.V sums.
+  float c2 = a.scale_log2e;
+  float v_scale = 1.f;
+  if constexpr (kFp8) {
+    c2 *= a.k_scale[g];
+    v_scale = a.v_scale[g];
+  }
 
   // ---- query operand ----
   // G >= 4: MFMA A operand; lane i holds head i%16 (zero when >= G) and the
   //         8 dims of chunk 4*kb + i/16 for k-block kb.
-  // G <= 2: lane i works on row i % kTile and the part i / kTile of D; it
+  // G <= 2: lane i works on row i % kT and the part i / kT of D; it
   //         holds that part of every head as bf16 pairs.
-  constexpr int kParts = 64 / kTile;
+  constexpr int kParts = 64 / kT;
   constexpr int kPartDims = D / kParts;
   bf16x8_t qa[kKBlocks];
   uint32_t qv[G <= 2 ? G : 1][G <= 2 ? kPartDims / 2 : 1];
@@ -280,7 +337,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       qa[kb] = as_bf16x8(w);
     }
   } else {
-    const int part = lane / kTile;
+    const int part = lane / kT;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4* qrow = reinterpret_cast<const uint4*>(
@@ -312,25 +369,41 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   // K goes from HBM straight into the wave's LDS tile (buffer_load ... lds):
   // load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the tile, lane l the
-  // 16 bytes at 16*l, i.e. row kRowsPerLoad*m + row_in_load, slot `chunk`.
+  // 16 bytes at 16*l, i.e. row kKRowsPerLoad*m + k_row_in_load, slot k_slot.
   // The lane fetches the logical chunk whose swizzled slot that is, so the
   // tile ends up in the k_tile_offset layout.  V goes to registers.
-  auto load_tile = [&](int r0, uint4* vr) {
+  using VReg = typename std::conditional<kFp8, uint2, uint4>::type;
+  auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf) {
     const int soff = r0 * kRowBytes;
 #pragma unroll
-    for (int m = 0; m < kLoads; ++m) {
-      const int r = kRowsPerLoad * m + row_in_load;
-      const int c = chunk ^ ((r / (256 / kRowBytes)) % kLanesPerRow);
+    for (int m = 0; m < kKLoads; ++m) {
+      const int r = kKRowsPerLoad * m + k_row_in_load;
+      const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(kt + m * 1024), 16,
+          rk, (__attribute__((address_space(3))) void*)(kbuf + m * 1024), 16,
           r * kRowBytes + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
     }
 #pragma unroll
-    for (int m = 0; m < kLoads; ++m)
-      vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+    for (int m = 0; m < kLoads; ++m) {
+      if constexpr (kFp8)
+        vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+      else
+        vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+    }
   };
 
-  auto process_tile = [&](int r0, const uint4* vr) {
+  // Elements 8*grp8 .. 8*grp8+7 of row r of a K tile, as bf16.
+  auto k_group = [&](const unsigned char* ktile, int r, int grp8) -> uint4 {
+    if constexpr (kFp8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(
+          ktile + k_tile_offset<kRowBytes>(r, grp8 >> 1) + 8 * (grp8 & 1));
+      return e4m3x8_to_bf16x8(w);
+    } else {
+      return *reinterpret_cast<const uint4*>(ktile + k_tile_offset<kRowBytes>(r, grp8));
+    }
+  };
+
+  auto process_tile = [&](int r0, const VReg* vr, const unsigned char* ktile) {
     // the K loads were issued before the V loads: wait for them only
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
     wave_lds_fence();
@@ -339,7 +412,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     bool grow = false;
     if constexpr (G >= 4) {
       constexpr int kHeadGroups = G / 4;
-      constexpr int kColGroups = kTile / 16;
+      constexpr int kColGroups = kT / 16;
       const int n = lane & 15;
       float x[kColGroups][4];
 #pragma unroll
@@ -347,8 +420,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < kKBlocks; ++kb) {
-          const uint4 kw = *reinterpret_cast<const uint4*>(
-              kt + k_tile_offset<D>(16 * tg + n, 4 * kb + (lane >> 4)));
+          const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + (lane >> 4));
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], as_bf16x8(kw), sacc, 0, 0, 0);
         }
         const bool ok = r0 + 16 * tg + n < row_end;
@@ -395,15 +467,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
               make_float4(x[tg][0], x[tg][1], x[tg][2], x[tg][3]);
       }
     } else {
-      // lane i: row i % kTile, part i / kTile of D; then add the parts
-      const int n = lane % kTile, part = lane / kTile;
+      // lane i: row i % kT, part i / kT of D; then add the parts
+      const int n = lane % kT, part = lane / kT;
       float x[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) x[h] = 0.f;
 #pragma unroll
       for (int cc = 0; cc < kPartDims / 8; ++cc) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(
-            kt + k_tile_offset<D>(n, part * (kPartDims / 8) + cc));
+        const uint4 kw = k_group(ktile, n, part * (kPartDims / 8) + cc);
         const uint32_t kwv[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -415,11 +486,11 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       const bool ok = r0 + n < row_end;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        x[h] = reduce_lane_bits<log2_int(kTile), false>(x[h]);  // add the parts of D
+        x[h] = reduce_lane_bits<log2_int(kT), false>(x[h]);  // add the parts of D
         x[h] = ok ? x[h] * c2 : -INFINITY;
         const float mt = row_reduce16<true>(x[h]);
         float tile_max = lane_value(mt, 0);
-        if constexpr (kTile == 32) tile_max = fmaxf(tile_max, lane_value(mt, 16));
+        if constexpr (kT == 32) tile_max = fmaxf(tile_max, lane_value(mt, 16));
         const float mn = fmaxf(m_run[h], tile_max);
         grow |= mn > m_run[h];
         alpha[h] = fast_exp2(m_run[h] - mn);
@@ -459,12 +530,16 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 #pragma unroll
         for (int h = 0; h < G; ++h) ph[h] = pt[r * G + h];
       }
-      const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
       float vf[8];
+      if constexpr (kFp8) {
+        e4m3x8_to_f32(vr[m], vf);
+      } else {
+        const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[2 * i] = bf16_lo(vw[i]);
-        vf[2 * i + 1] = bf16_hi(vw[i]);
+        for (int i = 0; i < 4; ++i) {
+          vf[2 * i] = bf16_lo(vw[i]);
+          vf[2 * i + 1] = bf16_hi(vw[i]);
+        }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -473,15 +548,15 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     }
   };
 
-  const int stride = kWaves * kTile;
-  for (int blk = s; blk < nb; blk += a.ns) {
-    const int row_lo = blk * a.chunk;
-    row_end = min(row_lo + a.chunk, L);
-    for (int r0 = row_lo + wave * kTile; r0 < row_end; r0 += stride) {
-      uint4 vr[kLoads];
-      load_tile(r0, vr);
-      process_tile(r0, vr);
-    }
+  // Split s streams rows [s * chunk, min((s + 1) * chunk, L)); wave w takes
+  // the tiles starting at w * kT, w * kT + kWaves * kT, ...
+  const int stride = kWaves * kT;
+  const int row_lo = s * a.chunk;
+  row_end = min(row_lo + a.chunk, L);
+  for (int r0 = row_lo + wave * kT; r0 < row_end; r0 += stride) {
+    VReg vr[kLoads];
+    load_tile(r0, vr, kt);
+    process_tile(r0, vr, kt);
   }
 
   // ---- end of the stream: each wave's state into its own tile region ----
@@ -507,7 +582,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float t = row_reduce16<false>(l_lane[h]);
-      l_tot[h] = lane_value(t, 0) + (kTile == 32 ? lane_value(t, 16) : 0.f);
+      l_tot[h] = lane_value(t, 0) + (kT == 32 ? lane_value(t, 16) : 0.f);
     }
   }
   // The wave's K tile and p buffer are no longer needed, and no other wave
@@ -591,6 +666,9 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       o.y = reduce_lane_bits<kGroupBit, false>(o.y);
       o.z = reduce_lane_bits<kGroupBit, false>(o.z);
       o.w = reduce_lane_bits<kGroupBit, false>(o.w);
+    }
+    if constexpr (kFp8) {
+      o.x *= v_scale; o.y *= v_scale; o.z *= v_scale; o.w *= v_scale;
     }
     if (rg == 0) {
       const size_t qh = qh0 + h;
@@ -865,13 +943,13 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool kFp8>
 static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipStream_t st) {
   // Dynamic LDS that brings the workgroup's total to kOnePerCuLds, more than
   // half a CU's LDS, so no second workgroup fits on the CU; a grid with no
   // more workgroups than CUs then spreads over all of them instead of
   // doubling up on some.  The static part already counts toward the total.
-  constexpr int kStatic = split_smem_bytes<D, G>() + kWaves * 2 * G * 4 + 64;  // + wave maxima/sums, scalars
+  constexpr int kStatic = split_smem_bytes<D, G, kFp8>() + kWaves * 2 * G * 4 + 64;
   static_assert(kStatic + 0 <= kMaxLdsPerWorkgroup, "static LDS over the limit");
   constexpr int kPad = kStatic < kOnePerCuLds ? kOnePerCuLds - kStatic : 0;
   static_assert(kStatic + kPad <= kMaxLdsPerWorkgroup, "padded LDS over the limit");
@@ -879,36 +957,43 @@ static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipSt
   // pure placement hint) if static + pad would not fit in a workgroup.
   static const int static_lds = [] {
     hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&split_kv_decode_kernel<D, G>)) !=
-        hipSuccess)
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
+                                      &split_kv_decode_kernel<D, G, kFp8>)) != hipSuccess)
       return -1;
     return (int)fa.sharedSizeBytes;
   }();
   const bool pad_fits = static_lds >= 0 && static_lds + kPad <= kMaxLdsPerWorkgroup;
   dim3 grid((unsigned)(a.ns | 1), (unsigned)a.Hkv, (unsigned)B);
-  hipLaunchKernelGGL((split_kv_decode_kernel<D, G>), grid, dim3(kThreads),
+  hipLaunchKernelGGL((split_kv_decode_kernel<D, G, kFp8>), grid, dim3(kThreads),
                      (unsigned)(one_per_cu && pad_fits ? kPad : 0), st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_split_kv_decode(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
-                                  hipStream_t st) {
+template <bool kFp8>
+static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
+                                     hipStream_t st) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch_split<128, 1>(B, a, one_per_cu, st);
-      case 2: return launch_split<128, 2>(B, a, one_per_cu, st);
-      case 4: return launch_split<128, 4>(B, a, one_per_cu, st);
-      case 8: return launch_split<128, 8>(B, a, one_per_cu, st);
+      case 1: return launch_split<128, 1, kFp8>(B, a, one_per_cu, st);
+      case 2: return launch_split<128, 2, kFp8>(B, a, one_per_cu, st);
+      case 4: return launch_split<128, 4, kFp8>(B, a, one_per_cu, st);
+      case 8: return launch_split<128, 8, kFp8>(B, a, one_per_cu, st);
     }
   } else if (D == 64) {
     switch (G) {
-      case 1: return launch_split<64, 1>(B, a, one_per_cu, st);
-      case 2: return launch_split<64, 2>(B, a, one_per_cu, st);
-      case 4: return launch_split<64, 4>(B, a, one_per_cu, st);
-      case 8: return launch_split<64, 8>(B, a, one_per_cu, st);
+      case 1: return launch_split<64, 1, kFp8>(B, a, one_per_cu, st);
+      case 2: return launch_split<64, 2, kFp8>(B, a, one_per_cu, st);
+      case 4: return launch_split<64, 4, kFp8>(B, a, one_per_cu, st);
+      case 8: return launch_split<64, 8, kFp8>(B, a, one_per_cu, st);
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_kv_decode(int D, int G, bool fp8, int B, const SplitArgs& a,
+                                  bool one_per_cu, hipStream_t st) {
+  return fp8 ? launch_split_typed<true>(D, G, B, a, one_per_cu, st)
+             : launch_split_typed<false>(D, G, B, a, one_per_cu, st);
 }
 
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st) {

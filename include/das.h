@@ -17,6 +17,9 @@
  *             chunk inflates phase-2 traffic, too large a chunk leaves
  *             compute units idle; aim for several times more blocks than
  *             compute units.
+ *             §4 ("quantisation-friendly kernel fusion"): an FP8 (or INT4) K/V
+ *             cache is dequantised on chip, right after it is loaded, back to
+ *             16-bit floats for the products, so fewer bytes cross HBM.
  *   [SGL-PAR] "병렬 처리 개요 (Parallelism Overview)", SGLang Diffusion docs.
  *             "What happens to the shapes" and "Constraints": partial
  *             attention results over disjoint row sets (ring hops, tail or
@@ -153,6 +156,39 @@ int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
                         int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
                         float* lse_out, int32_t num_splits, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over an 8-bit floating-point K/V cache ([FD++] §4).  The
+ * pages leave the FP8 encoding and its scaling open; this library reads them
+ * as OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * subnormals; S.1111.111 is NaN; no infinities) with one fp32 scale per
+ * kv-head for K and one for V:
+ *   K[b][g][j][d] = k_scale[g] * e4m3(k_cache[b][g][j][d]), V likewise.
+ *   k_cache, v_cache  uint8 E4M3 codes [B][Hkv][Smax][D]
+ *   k_scale, v_scale  device float [Hkv] (may point to one value repeated)
+ * Everything else (q, seq_lens, out, lse_out, num_splits, workspace and its
+ * precondition, stream, supported shapes, errors) is as for
+ * das_decode_attention; the plan and das_decode_workspace_bytes are shared.
+ * The codes are turned into bf16 (exactly) on chip for q.K^T and into fp32
+ * for p.V; the K scale multiplies the finished dot product and the V scale
+ * the finished p.V sums.  A sequence's rows are addressed with 32-bit byte
+ * offsets: (Smax + 256) * D < 2^31.  NULL k_scale or v_scale: DAS_EINVAL.
+ */
+int das_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                             float scale, void* out, int32_t out_dtype, float* lse_out,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Phase 1 alone over an E4M3 K/V cache: das_split_kv_decode with the cache
+ * of das_decode_attention_fp8.  Finish with das_lse_combine. */
+int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                            float scale, void* out, int32_t out_dtype, float* lse_out,
+                            int32_t num_splits, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * Phase 2 alone ([FD++] §3, phase 2): merges the partial results that

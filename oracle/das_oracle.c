@@ -270,7 +270,9 @@ void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t
                               const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                               int32_t Smax, int32_t D, double scale, double* out, double* lse) {
   const int G = Hq / Hkv;
-#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  double e4m3[256];  /* the value of every code, from e4m3_value */
+  for (int c = 0; c < 256; ++c) e4m3[c] = e4m3_value((uint8_t)c);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) firstprivate(e4m3)
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < Hq; ++h) {
       const int g = h / G;
@@ -290,7 +292,7 @@ void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t
       for (int j = 0; j < L; ++j) {
         const uint8_t* krow = kbase + (size_t)j * D;
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += widen_bf16(qrow[d]) * (ks * e4m3_value(krow[d]));
+        for (int d = 0; d < D; ++d) dot += widen_bf16(qrow[d]) * (ks * e4m3[krow[d]]);
         w[j] = scale * dot;
         if (w[j] > M) M = w[j];
       }
@@ -301,7 +303,7 @@ void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t
       }
       for (int j = 0; j < L; ++j) {
         const uint8_t* vrow = vbase + (size_t)j * D;
-        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * e4m3_value(vrow[d]));
+        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * e4m3[vrow[d]]);
       }
       for (int d = 0; d < D; ++d) o[d] /= Z;
       lse[(size_t)b * Hq + h] = M + log(Z);

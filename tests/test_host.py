@@ -132,6 +132,40 @@ def test_decode_argument_checks(lib, kw, status):
     assert _call_decode(lib, **kw) == status
 
 
+def _call_decode_fp8(lib, **kw):
+    a = dict(q=16, k=16, v=16, ks=16, vs=16, sl=16, B=1, Hq=8, Hkv=2, Smax=1024, D=128, scale=0.1,
+             out=16, dt=0, lse=0, ns=4, ws=16, wsb=1 << 30, st=None)
+    a.update(kw)
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.das_decode_attention_fp8(P(a["q"]), P(a["k"]), P(a["v"]), P(a["ks"]), P(a["vs"]),
+                                        P(a["sl"]), a["B"], a["Hq"], a["Hkv"], a["Smax"], a["D"],
+                                        a["scale"], P(a["out"]), a["dt"], P(a["lse"]), a["ns"],
+                                        P(a["ws"]), a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0), das.DAS_EINVAL), (dict(vs=0), das.DAS_EINVAL),
+    (dict(q=0), das.DAS_EINVAL), (dict(k=0), das.DAS_EINVAL), (dict(v=8), das.DAS_EINVAL),
+    (dict(Hq=6, Hkv=2), das.DAS_ENOTSUP), (dict(D=80), das.DAS_ENOTSUP),
+    (dict(ws=0), das.DAS_EWORKSPACE),
+    (dict(Smax=(1 << 24)), das.DAS_ENOTSUP),        # 32-bit row offsets: (Smax+256)*D >= 2^31
+])
+def test_decode_fp8_argument_checks(lib, kw, status):
+    # All pointers are fake: a failed check must return before any launch.
+    assert _call_decode_fp8(lib, **kw) == status
+    if "ks" not in kw and "vs" not in kw:   # the same checks as the bf16 entry point
+        assert _call_decode(lib, **kw) == status
+
+
+def test_fp8_row_bound_is_twice_the_bf16_one(lib):
+    # (Smax + 256) * D * bytes per element < 2^31: 1-byte codes allow twice the
+    # rows.  Both calls fail a check (no launch): the bf16 one on the row
+    # bound, the fp8 one only later, on the missing workspace.
+    smax = 1 << 23
+    assert _call_decode(lib, Smax=smax, ws=0) == das.DAS_ENOTSUP
+    assert _call_decode_fp8(lib, Smax=smax, ws=0) == das.DAS_EWORKSPACE
+
+
 def test_merge_argument_checks(lib):
     P = ctypes.c_void_p
     f = lib.das_merge_attn_states

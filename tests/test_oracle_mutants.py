@@ -41,8 +41,8 @@ MUTANTS = [
     ("e4m3_subnormal_as_normal", "v = ldexp((double)m, -9);", "v = ldexp(1.0 + (double)m / 8.0, -6);"),
     ("e4m3_no_nan", "if (e == 15 && m == 7) return NAN;", ""),
     ("e4m3_mantissa_over_16", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 16.0, e - 7);"),
-    ("fp8_k_scale_dropped", "(ks * e4m3_value(krow[d]))", "e4m3_value(krow[d])"),
-    ("fp8_v_scale_from_k", "(vs * e4m3_value(vrow[d]))", "(ks * e4m3_value(vrow[d]))"),
+    ("fp8_k_scale_dropped", "(ks * e4m3[krow[d]])", "e4m3[krow[d]]"),
+    ("fp8_v_scale_from_k", "(vs * e4m3[vrow[d]])", "(ks * e4m3[vrow[d]])"),
     ("fp8_scale_first_head", "const double ks = (double)k_scale[g]", "const double ks = (double)k_scale[0]"),
     ("split_chunk_off_by_one", "const int j1 = (j0 + chunk < L) ? j0 + chunk : L;",
      "const int j1 = (j0 + chunk < L) ? j0 + chunk - 1 : L;"),
