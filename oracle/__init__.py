@@ -20,6 +20,12 @@ Pieces:
   floating-point K/V cache (FlashDecoding++ post, §4: quantised K/V turned
   back into wider floats inside the kernel), read as OCP E4M3 codes with one
   fp32 scale per kv-head for K and one for V.
+* ``gather_paged`` / ``attention_paged`` -- a paged K/V cache (FlashDecoding++
+  post, §6: engines keep K/V in blocks allocated anywhere in a pool, listed
+  per sequence by a block table, and map each block onto a slice of a
+  chunk).  Row j of sequence b is row j mod P of block
+  ``block_table[b][j // P]``; the gather writes that out, and attention over
+  the paged cache is the definition above over the gathered rows.
 * ``merge`` -- the LSE / online-softmax merge of two attention states that
   the SGLang Diffusion "Parallelism Overview" page relies on for ring hops and
   tail parts ("What happens to the shapes", "Constraints").
@@ -207,6 +213,47 @@ def split_attention(q, k, v, seq_lens, scale: float, chunk: int):
 
 def merge(o_a, lse_a, o_b, lse_b):
     return default().merge(o_a, lse_a, o_b, lse_b)
+
+
+PAGED_HND = 0   # pool [num_pages][Hkv][P][D]
+PAGED_NHD = 1   # pool [num_pages][P][Hkv][D]
+
+
+def gather_paged(pool, block_table, seq_lens, page_size: int, layout: int, smax: int,
+                 fill) -> np.ndarray:
+    """Contiguous [B][Hkv][smax][D] copy of a paged cache: row j < seq_lens[b]
+    of kv-head g is row j % P of page block_table[b][j // P] (head g of it);
+    rows at or past seq_lens[b] hold ``fill``."""
+    pool = np.asarray(pool)
+    block_table = np.asarray(block_table)
+    if layout == PAGED_HND:
+        _, Hkv, P, D = pool.shape
+    elif layout == PAGED_NHD:
+        _, P, Hkv, D = pool.shape
+    else:
+        raise ValueError("layout must be PAGED_HND or PAGED_NHD")
+    if P != page_size:
+        raise ValueError("pool page size differs from page_size")
+    B = len(seq_lens)
+    out = np.full((B, Hkv, smax, D), fill, dtype=pool.dtype)
+    for b in range(B):
+        for j in range(int(seq_lens[b])):
+            page = int(block_table[b][j // P])
+            r = j % P
+            if layout == PAGED_HND:
+                out[b, :, j, :] = pool[page, :, r, :]
+            else:
+                out[b, :, j, :] = pool[page, r, :, :]
+    return out
+
+
+def attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, layout: int,
+                    scale: float, lib=None):
+    """fp64 attention over a paged bf16 cache: the definition over the gathered rows."""
+    smax = int(np.asarray(block_table).shape[1]) * page_size
+    k = gather_paged(k_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
+    v = gather_paged(v_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
+    return (lib or default()).attention(q, k, v, seq_lens, scale)
 
 
 def e4m3_decode(codes):

@@ -410,6 +410,51 @@ def pin_fp8_bruteforce_tiny(lib):
         assert abs(l[0, h] - rl) <= 1e-12 * max(1.0, abs(rl)), f"lse head {h}"
 
 
+# ---- paged K/V cache: FlashDecoding++ post §6 ----
+
+def pin_paged_gather_inverts_the_generators_scatter(lib):
+    """The generator scatters rows into a shuffled page pool with its own code;
+    the oracle's gather must give back exactly the contiguous rows (and the
+    fill value beyond each sequence), for both pool layouts and several page
+    sizes, with spare pages in the pool and in the table."""
+    cfg = workloads.custom_config(4, 8, 2, 16, 200)
+    for P in (32, 64):
+        for layout in (oracle.PAGED_HND, oracle.PAGED_NHD):
+            x = workloads.make_paged_inputs(cfg, 31 + P + layout, P, layout, seq_lens=(200, 1, 64, 0))
+            smax = x.block_table.shape[1] * P
+            for pool, ref in ((x.k_pool, x.base.k), (x.v_pool, x.base.v)):
+                got = oracle.gather_paged(pool, x.block_table, x.base.seq_lens, P, layout, smax, 7)
+                for b, L in enumerate(x.base.seq_lens):
+                    assert np.array_equal(got[b, :, :L], ref[b, :, :L]), f"P={P} layout={layout} b={b}"
+                    assert np.all(got[b, :, L:] == 7), "rows past the sequence must be the fill"
+
+
+def pin_paged_identity_table_is_a_reshape(lib):
+    """With block_table[b][i] = b * max_blocks + i, an HND pool is the
+    contiguous cache reshaped, and an NHD pool that with rows and heads
+    swapped (numpy reshape / transpose)."""
+    rng = np.random.default_rng(5)
+    B, Hkv, P, nb, D = 2, 3, 32, 4, 8
+    cache = rng.integers(0, 1 << 16, size=(B, Hkv, nb * P, D), dtype=np.uint16)
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    lens = np.array([nb * P, nb * P], dtype=np.int32)
+    hnd = cache.reshape(B, Hkv, nb, P, D).transpose(0, 2, 1, 3, 4).reshape(B * nb, Hkv, P, D)
+    nhd = hnd.transpose(0, 2, 1, 3)
+    assert np.array_equal(oracle.gather_paged(hnd, table, lens, P, oracle.PAGED_HND, nb * P, 0), cache)
+    assert np.array_equal(oracle.gather_paged(nhd, table, lens, P, oracle.PAGED_NHD, nb * P, 0), cache)
+
+
+def pin_paged_attention_equals_contiguous(lib):
+    """Attention over the paged cache is bitwise the (pinned) contiguous
+    definition over the same rows."""
+    cfg = workloads.custom_config(3, 8, 2, 32, 150)
+    x = workloads.make_paged_inputs(cfg, 41, 32, oracle.PAGED_NHD, seq_lens=(150, 33, 0))
+    o, l = oracle.attention_paged(x.base.q, x.k_pool, x.v_pool, x.block_table, x.base.seq_lens,
+                                  32, oracle.PAGED_NHD, x.base.scale, lib=lib)
+    ro, rl = lib.attention(x.base.q, x.base.k, x.base.v, x.base.seq_lens, x.base.scale)
+    assert np.array_equal(o, ro) and np.array_equal(l, rl)
+
+
 ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_") and callable(v)),
                   key=lambda f: (f is pin_fd_equivalence_check, f.__name__))
 

@@ -23,6 +23,12 @@ Recipe (one config = one seed, ``seed = 42 + config index``):
   (0x7FC0) so that any kernel reading them contaminates its result.
 * ``scale = 1/sqrt(D)`` rounded to float32 (the library takes a float).
 
+Paged caches (``make_paged_inputs``): the contiguous bf16 draw above, then
+every sequence's rows are cut into pages of P rows and the pages are placed
+in a pool in an order given by ``PCG64(seed + 7919).permutation``; the pool
+also holds a few spare pages (all NaN) that no table points to, and the
+block-table entries past a sequence's last page point to a spare page.
+
 8-bit (E4M3) K/V caches (``make_fp8_inputs``): q as above; per kv-head
 scales ``k_scale[g] = k_mult * (4 + g) / 64`` and ``v_scale[g] = (3 + g) / 64``
 (float32); the codes of K (``t = 2``) and V (``t = 3``) of batch row ``b``,
@@ -282,3 +288,58 @@ def make_fp8_inputs(cfg: Config, seed: int, smax: Optional[int] = None,
 def config_fp8_inputs(index: int) -> Fp8Inputs:
     """The named config ``index`` at its full size with an E4M3 cache, seed 42 + index."""
     return make_fp8_inputs(CONFIGS[index], 42 + index)
+
+
+PAGED_HND = 0   # pool [num_pages][Hkv][P][D]
+PAGED_NHD = 1   # pool [num_pages][P][Hkv][D]
+
+
+@dataclasses.dataclass
+class PagedInputs:
+    base: Inputs              # the same rows as a contiguous cache
+    page_size: int
+    layout: int
+    k_pool: np.ndarray        # uint16, [num_pages][Hkv][P][D] (HND) or [num_pages][P][Hkv][D] (NHD)
+    v_pool: np.ndarray
+    block_table: np.ndarray   # int32 [B][max_blocks]
+
+    @property
+    def kv_bytes(self) -> int:
+        return self.base.kv_bytes
+
+
+def make_paged_inputs(cfg: Config, seed: int, page_size: int, layout: int = PAGED_HND,
+                      smax: Optional[int] = None, seq_lens: Optional[Sequence[int]] = None,
+                      spare_pages: int = 3) -> PagedInputs:
+    """``make_inputs`` (same seed, same rows), scattered into a page pool."""
+    base = make_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+    B, Hkv, S, D = base.k.shape
+    P = int(page_size)
+    max_blocks = (S + P - 1) // P
+    used = [(int(L) + P - 1) // P for L in base.seq_lens]
+    n_used = int(sum(used))
+    num_pages = n_used + spare_pages
+    order = np.random.Generator(np.random.PCG64(seed + 7919)).permutation(num_pages)
+    spare = [int(p) for p in order[n_used:]] or [0]
+    table = np.empty((B, max_blocks), dtype=np.int32)
+    shape = (num_pages, Hkv, P, D) if layout == PAGED_HND else (num_pages, P, Hkv, D)
+    k_pool = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    v_pool = np.full(shape, BF16_QNAN, dtype=np.uint16)
+    nxt = 0
+    for b in range(B):
+        L = int(base.seq_lens[b])
+        for i in range(max_blocks):
+            if i < used[b]:
+                page = int(order[nxt])
+                nxt += 1
+                j0, j1 = i * P, min(L, (i + 1) * P)
+                for src, pool in ((base.k, k_pool), (base.v, v_pool)):
+                    rows = src[b, :, j0:j1, :]                     # [Hkv][n][D]
+                    if layout == PAGED_HND:
+                        pool[page, :, : j1 - j0, :] = rows
+                    else:
+                        pool[page, : j1 - j0, :, :] = rows.transpose(1, 0, 2)
+                table[b, i] = page
+            else:
+                table[b, i] = spare[i % len(spare)]
+    return PagedInputs(base, P, layout, k_pool, v_pool, table)
