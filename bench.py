@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="K/V cache element: bf16, or E4M3 codes with per-kv-head scales")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="page size in rows: time the paged entry point over a shuffled pool")
+    ap.add_argument("--paged-layout", choices=("hnd", "nhd"), default="hnd")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate; 0 = auto")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline; 0 skips it")
@@ -159,11 +162,23 @@ def main():
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.config]
     fp8 = args.kv_dtype == "fp8"
-    x = workloads.config_fp8_inputs(args.config) if fp8 else workloads.config_inputs(args.config)
+    paged = None
+    if args.paged:
+        layout = workloads.PAGED_HND if args.paged_layout == "hnd" else workloads.PAGED_NHD
+        paged = workloads.make_paged_inputs(cfg, 42 + args.config, args.paged, layout, fp8=fp8)
+        x = paged.base
+    else:
+        x = workloads.config_fp8_inputs(args.config) if fp8 else workloads.config_inputs(args.config)
     B, Hq, D = x.q.shape
     Hkv, Smax = x.k.shape[1], x.k.shape[2]
     kv_bytes = x.kv_bytes
+    if paged is not None:
+        # the paged plan: Smax = max_blocks * page size, chunks rounded up to whole pages
+        Smax = paged.block_table.shape[1] * paged.page_size
     ns, chunk = das.das_plan(B, Hkv, Hq // Hkv, Smax, D, args.splits)
+    if paged is not None and chunk % paged.page_size:
+        chunk = -(-chunk // paged.page_size) * paged.page_size
+        ns = -(-Smax // chunk)
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -172,11 +187,18 @@ def main():
     sl = torch.from_numpy(x.seq_lens).to(dev)
     alloc = x.k.nbytes + x.v.nbytes
     copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
+    k_scale = v_scale = None
     if fp8:
-        k0, v0 = torch.from_numpy(x.k).to(dev), torch.from_numpy(x.v).to(dev)
         k_scale, v_scale = torch.from_numpy(x.k_scale).to(dev), torch.from_numpy(x.v_scale).to(dev)
+    src_k, src_v = (paged.k_pool, paged.v_pool) if paged is not None else (x.k, x.v)
+    if fp8:
+        k0, v0 = torch.from_numpy(src_k).to(dev), torch.from_numpy(src_v).to(dev)
     else:
-        k0, v0 = up(x.k), up(x.v)
+        k0, v0 = up(src_k), up(src_v)
+    if paged is not None:
+        alloc = paged.k_pool.nbytes + paged.v_pool.nbytes
+        copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
+        table = torch.from_numpy(paged.block_table).to(dev)
     ks, vs = [k0], [v0]
     for _ in range(copies - 1):
         ks.append(k0.clone())
@@ -190,7 +212,12 @@ def main():
     # One prepared decode-attention call per K/V copy.  It is a single kernel
     # launch: phase 1 plus the fused phase-2 merge by the last workgroup of
     # each (b, kv-head).
-    if fp8:
+    if paged is not None:
+        calls = [das.prepare_decode_paged(q, ks[c], vs[c], table, sl, x.scale, paged.page_size,
+                                          paged.layout, out, lse, args.splits, ws,
+                                          k_scale=k_scale, v_scale=v_scale)
+                 for c in range(copies)]
+    elif fp8:
         calls = [das.prepare_decode("das_decode_attention_fp8", q, ks[c], vs[c], sl, x.scale, out,
                                     lse, args.splits, ws, k_scale=k_scale, v_scale=v_scale)
                  for c in range(copies)]
@@ -241,6 +268,8 @@ def main():
             "num_splits": ns, "chunk": chunk,
             "out_dtype": args.out_dtype,
             "kv_dtype": args.kv_dtype,
+            "paged": ({"page_size": paged.page_size, "layout": args.paged_layout}
+                      if paged is not None else None),
             "kv_copies_rotated": copies,
             "us_per_call": round(ms_per_step * 1e3, 2),
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -252,11 +281,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if fp8 else measured_traffic(cfg.name, ns),
+            "traffic": None if (fp8 or paged is not None) else measured_traffic(cfg.name, ns),
             "kernel_us": round(kernel_ms * 1e3, 3),
         },
     }
-    if args.cpu_seconds > 0 and not fp8:
+    if args.cpu_seconds > 0 and not fp8 and paged is None:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -19,14 +19,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdas.so")
 
 DAS_OK, DAS_EINVAL, DAS_ENOTSUP, DAS_EWORKSPACE, DAS_ELAUNCH = 0, -1, -2, -3, -4
-DAS_F32, DAS_BF16 = 0, 1
+DAS_F32, DAS_BF16, DAS_E4M3 = 0, 1, 2
+DAS_PAGED_HND, DAS_PAGED_NHD = 0, 1
 DAS_MAX_SPLITS = 4096
 DAS_CHUNK_QUANTUM = 128
 DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 
 EXPORTED = ("das_plan", "das_decode_workspace_bytes", "das_decode_attention",
             "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
-            "das_lse_combine", "das_merge_attn_states", "das_strerror")
+            "das_decode_attention_paged", "das_lse_combine", "das_merge_attn_states",
+            "das_strerror")
 
 _lib = None
 
@@ -60,6 +62,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8"):
         getattr(lib, name).argtypes = fp8_args
         getattr(lib, name).restype = ctypes.c_int
+    lib.das_decode_attention_paged.argtypes = [p, p, p, i32, p, p, p, i32, i32, i32, i32, p, i32,
+                                               i32, i32, i32, ctypes.c_float, p, i32, p, i32, p,
+                                               sz, p]
+    lib.das_decode_attention_paged.restype = ctypes.c_int
     lib.das_lse_combine.argtypes = [p, i32, i32, i32, i32, i32, i32, p, sz, p, i32, p, p]
     lib.das_lse_combine.restype = ctypes.c_int
     lib.das_merge_attn_states.argtypes = [p, p, p, p, p, p, i64, i32, i32, p]
@@ -275,6 +281,72 @@ def das_split_kv_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, sca
     return _run_decode_fp8("das_split_kv_decode_fp8", q, k_cache, v_cache, k_scale, v_scale,
                            seq_lens, scale, out, lse_out, out_dtype, num_splits, workspace,
                            stream, with_lse)
+
+
+def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layout, k_scale,
+                v_scale, out, lse_out, out_dtype, num_splits, workspace, stream, with_lse):
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or q.dim() != 3:
+        raise ValueError("q must be bfloat16 [B,Hq,D]")
+    if k_pool.dtype == torch.bfloat16:
+        kv_dtype = DAS_BF16
+    elif k_pool.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kv_dtype = DAS_E4M3
+    else:
+        raise ValueError("page pools must be bfloat16, or E4M3 codes (uint8 / float8_e4m3fn)")
+    if v_pool.dtype != k_pool.dtype or v_pool.shape != k_pool.shape or k_pool.dim() != 4:
+        raise ValueError("k_pool and v_pool must share one 4-d shape and dtype")
+    B, Hq, D = q.shape
+    if layout == DAS_PAGED_HND:
+        num_pages, Hkv, P, Dk = k_pool.shape
+    elif layout == DAS_PAGED_NHD:
+        num_pages, P, Hkv, Dk = k_pool.shape
+    else:
+        raise ValueError("layout must be DAS_PAGED_HND or DAS_PAGED_NHD")
+    if P != page_size or Dk != D:
+        raise ValueError("pool shape disagrees with page_size or D")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if kv_dtype == DAS_E4M3:
+        _scales(k_scale, v_scale, Hkv)
+    max_blocks = block_table.shape[1]
+    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, max_blocks * P, D, num_splits, workspace)
+    code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), kv_dtype, _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_table), max_blocks, P, num_pages, layout, _ptr(seq_lens), B, Hq, Hkv, D,
+            ctypes.c_float(scale), _ptr(out), code, _ptr(lse_out), int(num_splits),
+            _ptr(workspace), ws_bytes, _stream(stream))
+    keep = (q, k_pool, v_pool, block_table, seq_lens, out, lse_out, workspace, k_scale, v_scale)
+    return args, keep, out, lse_out
+
+
+def das_decode_attention_paged(q, k_pool, v_pool, block_table, seq_lens, scale, page_size,
+                               layout=0, k_scale=None, v_scale=None, out=None, lse_out=None,
+                               out_dtype=torch.float32, num_splits=0, workspace=None, stream=None,
+                               with_lse=True):
+    """Decode attention over a paged cache (bf16 or E4M3 page pools, int32 block
+    table [B, max_blocks]); returns (out, lse)."""
+    args, _, out, lse_out = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale,
+                                        page_size, layout, k_scale, v_scale, out, lse_out,
+                                        out_dtype, num_splits, workspace, stream, with_lse)
+    _check(load_library().das_decode_attention_paged(*args), "das_decode_attention_paged")
+    return out, lse_out
+
+
+def prepare_decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layout,
+                         out, lse_out, num_splits, workspace, stream=None, k_scale=None,
+                         v_scale=None) -> "PreparedCall":
+    """Prepared das_decode_attention_paged call (same checks once)."""
+    args, keep, _, _ = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size,
+                                   layout, k_scale, v_scale, out, lse_out, out.dtype, num_splits,
+                                   workspace, stream, lse_out is not None)
+    return PreparedCall("das_decode_attention_paged", args, keep)
 
 
 def das_lse_combine(seq_lens: torch.Tensor, Hq: int, Hkv: int, Smax: int, D: int,

@@ -130,13 +130,18 @@ struct KvCache {
   const float* k_scale;
   const float* v_scale;
   bool fp8;
+  // paged cache (FlashDecoding++ post, §6): k and v are page pools
+  const int32_t* block_table = nullptr;
+  int32_t max_blocks = 0, page_size = 0, num_pages = 0, layout = 0;
+  bool paged() const { return block_table != nullptr; }
   int elem_bytes() const { return fp8 ? 1 : 2; }
 };
 
 int check_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
                  int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, const void* out,
                  int32_t out_dtype, int32_t num_splits, const void* workspace,
-                 size_t workspace_bytes, bool need_inputs, int elem_bytes, Checked* c) {
+                 size_t workspace_bytes, bool need_inputs, int elem_bytes, Checked* c,
+                 int32_t page_size = 0) {
   if (seq_lens == nullptr || out == nullptr) return DAS_EINVAL;
   if (need_inputs && (q == nullptr || k == nullptr || v == nullptr)) return DAS_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || D < 1) return DAS_EINVAL;
@@ -147,12 +152,18 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   if (!supported_dims(D, G)) return DAS_ENOTSUP;
   // a sequence's K (or V) rows, plus one tile of overhang, are addressed
   // with 32-bit byte offsets
-  if ((int64_t)(Smax + 256) * D * elem_bytes > INT32_MAX) return DAS_ENOTSUP;
+  if (page_size == 0 && (int64_t)(Smax + 256) * D * elem_bytes > INT32_MAX) return DAS_ENOTSUP;
   if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
   if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
   int32_t ns = 0, chunk = 0;
   const int rc = plan_impl(B, Hkv, G, Smax, D, num_splits, 0, &ns, &chunk);
   if (rc != DAS_OK) return rc;
+  if (page_size > 0 && chunk % page_size != 0) {
+    // a paged cache's chunks are whole pages: fewer, longer splits, so the
+    // workspace the unpaged plan asks for is enough
+    chunk = (int32_t)(((int64_t)chunk + page_size - 1) / page_size * page_size);
+    ns = (int32_t)(((int64_t)Smax + chunk - 1) / chunk);
+  }
   if (ns > 1) {
     if (workspace == nullptr || !aligned16(workspace)) return DAS_EWORKSPACE;
     if (workspace_bytes < ws_total(B, Hq, ns, D)) return DAS_EWORKSPACE;
@@ -172,6 +183,23 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   a.v = kv.v;
   a.k_scale = kv.k_scale;
   a.v_scale = kv.v_scale;
+  if (kv.paged()) {
+    const int E = kv.elem_bytes();
+    int shift = 0;
+    while ((1 << shift) < kv.page_size) ++shift;
+    a.block_table = kv.block_table;
+    a.max_blocks = kv.max_blocks;
+    a.page_shift = shift;
+    a.num_pages = kv.num_pages;
+    a.page_bytes = (int64_t)kv.page_size * Hkv * D * E;
+    if (kv.layout == DAS_PAGED_HND) {
+      a.row_stride = D * E;
+      a.head_stride = kv.page_size * D * E;
+    } else {
+      a.row_stride = Hkv * D * E;
+      a.head_stride = D * E;
+    }
+  }
   a.seq_lens = seq_lens;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -194,7 +222,8 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   int cus = 0;
   if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
   const bool one_per_cu = DAS_ONE_PER_CU && (int64_t)B * Hkv * c.ns <= cus;
-  return das::launch_split_kv_decode(D, c.G, kv.fp8, B, a, one_per_cu, st) == hipSuccess
+  return das::launch_split_kv_decode(D, c.G, kv.fp8, kv.paged(), B, a, one_per_cu, st) ==
+                 hipSuccess
              ? DAS_OK
              : DAS_ELAUNCH;
 }
@@ -236,7 +265,8 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
                 void* stream) {
   Checked c{};
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
-                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c);
+                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c,
+                              kv.page_size);
   if (rc != DAS_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One launch: the last workgroup of each (b, kv-head) merges the splits.
@@ -329,6 +359,35 @@ int das_decode_attention_fp8(const void* q, const void* k_cache, const void* v_c
   const KvCache kv{k_cache, v_cache, k_scale, v_scale, true};
   return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                      num_splits, workspace, workspace_bytes, stream);
+}
+
+int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
+                               int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, int32_t max_blocks, int32_t page_size,
+                               int32_t num_pages, int32_t layout, const int32_t* seq_lens,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                               void* out, int32_t out_dtype, float* lse_out, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_dtype != DAS_BF16 && kv_dtype != DAS_E4M3) return DAS_EINVAL;
+  const bool fp8 = kv_dtype == DAS_E4M3;
+  if (fp8 && (k_scale == nullptr || v_scale == nullptr)) return DAS_EINVAL;
+  if (block_table == nullptr || ((uintptr_t)block_table & 3u) != 0) return DAS_EINVAL;
+  if (layout != DAS_PAGED_HND && layout != DAS_PAGED_NHD) return DAS_EINVAL;
+  if (max_blocks < 1 || num_pages < 1) return DAS_EINVAL;
+  if (page_size < 32 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
+    return DAS_ENOTSUP;
+  if ((int64_t)max_blocks * page_size > INT32_MAX) return DAS_EINVAL;
+  // one page's rows of one kv-head are addressed with 32-bit byte offsets
+  const int64_t E = fp8 ? 1 : 2;
+  if ((int64_t)page_size * Hkv * D * E > INT32_MAX) return DAS_ENOTSUP;
+  KvCache kv{k_pool, v_pool, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, fp8};
+  kv.block_table = block_table;
+  kv.max_blocks = max_blocks;
+  kv.page_size = page_size;
+  kv.num_pages = num_pages;
+  kv.layout = layout;
+  return decode_impl(q, kv, seq_lens, B, Hq, Hkv, max_blocks * page_size, D, scale, out, out_dtype,
+                     lse_out, num_splits, workspace, workspace_bytes, stream);
 }
 
 int das_merge_attn_states(const void* o_a, const float* lse_a, const void* o_b,

@@ -50,6 +50,15 @@ struct SplitArgs {
   int32_t direct;            // 1: single split, write out/lse instead of partials
   int32_t fused;             // 1: the last workgroup of each (b, kv-head) merges the splits
   unsigned int* counters;    // fused: arrival counters [B][Hkv], zero between calls
+  // Paged cache (FlashDecoding++ post, §6): k and v point to page pools and
+  // row j of sequence b is row j mod P of page block_table[b][j / P].
+  const int32_t* block_table;  // [B][max_blocks]
+  int32_t max_blocks;
+  int32_t page_shift;        // log2 P, P >= 32 rows
+  int32_t num_pages;         // pool size; table entries are clamped to it
+  int32_t row_stride;        // bytes between rows of one kv-head within a page
+  int32_t head_stride;       // bytes between kv-heads within a page
+  int64_t page_bytes;        // bytes per page (every kv-head)
 };
 
 // Arrival counters live at the start of the workspace, one per (batch row,
@@ -85,7 +94,7 @@ struct MergeArgs {
 // a second one on its CU.
 constexpr int kMaxLdsPerWorkgroup = 160 * 1024;
 constexpr int kOnePerCuLds = 84 * 1024;
-hipError_t launch_split_kv_decode(int D, int G, bool fp8, int B, const SplitArgs& a,
+hipError_t launch_split_kv_decode(int D, int G, bool fp8, bool paged, int B, const SplitArgs& a,
                                   bool one_per_cu, hipStream_t stream);
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
 hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t stream);

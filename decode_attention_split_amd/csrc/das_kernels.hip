@@ -235,8 +235,11 @@ constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
 // Phase 1: split_kv_decode.  Grid (ns | 1, Hkv, B), kThreads threads.
 // kFp8: K and V are E4M3 codes with one fp32 scale per kv-head each
 // (FlashDecoding++ post, §4), dequantised on chip; otherwise bf16.
+// kPaged: K and V live in page pools listed by a block table (same post,
+// §6); a tile never straddles a page (pages are >= 32 rows, chunks whole
+// pages), so every tile finds its page with one table entry.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool kFp8>
+template <int D, int G, bool kFp8, bool kPaged>
 __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     void split_kv_decode_kernel(SplitArgs a) {
   constexpr int kElemBytes = kFp8 ? 1 : 2;
@@ -296,15 +299,20 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   // The sequence's valid rows of K and V as bounds-checked buffers: loads
   // past row L return zeros, and the rows beyond seq_lens are never read.
-  const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax * kRowBytes;  // bytes
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + slab, L * kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + slab, L * kRowBytes);
-  int row_end = 0;                              // end of the block being streamed
+  // Contiguous cache: the sequence's valid rows as one bounds-checked
+  // buffer.  Paged cache: a buffer per tile over its page's valid rows.
+  // Either way loads past the last valid row return zeros and the rows
+  // beyond seq_lens are never read.
+  const int row_stride = kPaged ? a.row_stride : kRowBytes;  // bytes between rows
+  const size_t slab = kPaged ? 0 : ((size_t)b * a.Hkv + g) * (size_t)a.Smax * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk_seq =
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + slab, kPaged ? 0 : L * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv_seq =
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + slab, kPaged ? 0 : L * kRowBytes);
+  int row_end = 0;                              // end of the chunk being streamed
   const int row_in_load = lane / kLanesPerRow;  // this lane's V row within a load
   const int chunk = lane % kLanesPerRow;        // this lane's 8 elements of a V row
-  const int lane_off = row_in_load * kRowBytes + kVLaneBytes * chunk;
+  const int lane_off = row_in_load * row_stride + kVLaneBytes * chunk;
   const int k_row_in_load = lane / kKLanesPerRow;
   const int k_slot = lane % kKLanesPerRow;
   // Logits in base-2 units; an E4M3 cache's K scale multiplies the finished
@@ -373,22 +381,46 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   // The lane fetches the logical chunk whose swizzled slot that is, so the
   // tile ends up in the k_tile_offset layout.  V goes to registers.
   using VReg = typename std::conditional<kFp8, uint2, uint4>::type;
-  auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf) {
-    const int soff = r0 * kRowBytes;
+  // Paged cache: the block-table entry of the page holding row r.  The table
+  // is read-only for the whole kernel, so it is read through the constant
+  // address space, which makes this a scalar load that only its use waits
+  // for; the stream loop fetches the next tile's entry one tile ahead.
+  auto page_of = [&](int r) -> int {
+    const __attribute__((address_space(4))) int32_t* table =
+        (const __attribute__((address_space(4))) int32_t*)a.block_table;
+    return table[(size_t)b * a.max_blocks + (r >> a.page_shift)];
+  };
+
+  auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf, int page) {
+    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
+    int soff = r0 * kRowBytes;
+    if constexpr (kPaged) {
+      // this tile's page; a table entry outside the pool is clamped into it
+      // (wrong rows, never an access outside the pool)
+      const int slot = r0 >> a.page_shift;
+      page = min(max(page, 0), a.num_pages - 1);
+      const int p0 = slot << a.page_shift;                  // first row of the page
+      const int nvalid = min(L - p0, 1 << a.page_shift);    // >= 1: r0 < L
+      const size_t off = (size_t)page * (size_t)a.page_bytes + (size_t)g * (size_t)a.head_stride;
+      const int bytes = (nvalid - 1) * row_stride + kRowBytes;
+      rk = make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + off, bytes);
+      rv = make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + off, bytes);
+      soff = (r0 - p0) * row_stride;
+    }
 #pragma unroll
     for (int m = 0; m < kKLoads; ++m) {
       const int r = kKRowsPerLoad * m + k_row_in_load;
       const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rk, (__attribute__((address_space(3))) void*)(kbuf + m * 1024), 16,
-          r * kRowBytes + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
+          r * row_stride + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
     }
 #pragma unroll
     for (int m = 0; m < kLoads; ++m) {
       if constexpr (kFp8)
-        vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+        vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
       else
-        vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * kRowBytes, soff);
+        vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
     }
   };
 
@@ -553,9 +585,13 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int stride = kWaves * kT;
   const int row_lo = s * a.chunk;
   row_end = min(row_lo + a.chunk, L);
-  for (int r0 = row_lo + wave * kT; r0 < row_end; r0 += stride) {
+  int r0 = row_lo + wave * kT;
+  int page_next = (kPaged && r0 < row_end) ? page_of(r0) : 0;
+  for (; r0 < row_end; r0 += stride) {
+    const int page = page_next;
+    if (kPaged && r0 + stride < row_end) page_next = page_of(r0 + stride);
     VReg vr[kLoads];
-    load_tile(r0, vr, kt);
+    load_tile(r0, vr, kt, page);
     process_tile(r0, vr, kt);
   }
 
@@ -943,7 +979,7 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, int G, bool kFp8>
+template <int D, int G, bool kFp8, bool kPaged>
 static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipStream_t st) {
   // Dynamic LDS that brings the workgroup's total to kOnePerCuLds, more than
   // half a CU's LDS, so no second workgroup fits on the CU; a grid with no
@@ -958,42 +994,45 @@ static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipSt
   static const int static_lds = [] {
     hipFuncAttributes fa;
     if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
-                                      &split_kv_decode_kernel<D, G, kFp8>)) != hipSuccess)
+                                      &split_kv_decode_kernel<D, G, kFp8, kPaged>)) != hipSuccess)
       return -1;
     return (int)fa.sharedSizeBytes;
   }();
   const bool pad_fits = static_lds >= 0 && static_lds + kPad <= kMaxLdsPerWorkgroup;
   dim3 grid((unsigned)(a.ns | 1), (unsigned)a.Hkv, (unsigned)B);
-  hipLaunchKernelGGL((split_kv_decode_kernel<D, G, kFp8>), grid, dim3(kThreads),
+  hipLaunchKernelGGL((split_kv_decode_kernel<D, G, kFp8, kPaged>), grid, dim3(kThreads),
                      (unsigned)(one_per_cu && pad_fits ? kPad : 0), st, a);
   return hipGetLastError();
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kPaged>
 static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
                                      hipStream_t st) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch_split<128, 1, kFp8>(B, a, one_per_cu, st);
-      case 2: return launch_split<128, 2, kFp8>(B, a, one_per_cu, st);
-      case 4: return launch_split<128, 4, kFp8>(B, a, one_per_cu, st);
-      case 8: return launch_split<128, 8, kFp8>(B, a, one_per_cu, st);
+      case 1: return launch_split<128, 1, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 2: return launch_split<128, 2, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 4: return launch_split<128, 4, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 8: return launch_split<128, 8, kFp8, kPaged>(B, a, one_per_cu, st);
     }
   } else if (D == 64) {
     switch (G) {
-      case 1: return launch_split<64, 1, kFp8>(B, a, one_per_cu, st);
-      case 2: return launch_split<64, 2, kFp8>(B, a, one_per_cu, st);
-      case 4: return launch_split<64, 4, kFp8>(B, a, one_per_cu, st);
-      case 8: return launch_split<64, 8, kFp8>(B, a, one_per_cu, st);
+      case 1: return launch_split<64, 1, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 2: return launch_split<64, 2, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 4: return launch_split<64, 4, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 8: return launch_split<64, 8, kFp8, kPaged>(B, a, one_per_cu, st);
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_split_kv_decode(int D, int G, bool fp8, int B, const SplitArgs& a,
+hipError_t launch_split_kv_decode(int D, int G, bool fp8, bool paged, int B, const SplitArgs& a,
                                   bool one_per_cu, hipStream_t st) {
-  return fp8 ? launch_split_typed<true>(D, G, B, a, one_per_cu, st)
-             : launch_split_typed<false>(D, G, B, a, one_per_cu, st);
+  if (paged)
+    return fp8 ? launch_split_typed<true, true>(D, G, B, a, one_per_cu, st)
+               : launch_split_typed<false, true>(D, G, B, a, one_per_cu, st);
+  return fp8 ? launch_split_typed<true, false>(D, G, B, a, one_per_cu, st)
+             : launch_split_typed<false, false>(D, G, B, a, one_per_cu, st);
 }
 
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st) {

@@ -20,6 +20,9 @@
  *             §4 ("quantisation-friendly kernel fusion"): an FP8 (or INT4) K/V
  *             cache is dequantised on chip, right after it is loaded, back to
  *             16-bit floats for the products, so fewer bytes cross HBM.
+ *             §6 (vLLM / TensorRT-LLM integration): serving engines keep K/V
+ *             in blocks allocated anywhere in a pool, listed per sequence by a
+ *             block table, and map each block onto a slice of a split's chunk.
  *   [SGL-PAR] "병렬 처리 개요 (Parallelism Overview)", SGLang Diffusion docs.
  *             "What happens to the shapes" and "Constraints": partial
  *             attention results over disjoint row sets (ring hops, tail or
@@ -70,7 +73,15 @@ typedef enum {
   DAS_ELAUNCH = -4,    /* the HIP runtime refused a launch or a device query */
 } das_status;
 
-typedef enum { DAS_F32 = 0, DAS_BF16 = 1 } das_dtype;
+/* Element types.  Outputs are DAS_F32 or DAS_BF16; a K/V cache is DAS_BF16
+ * or DAS_E4M3 (OCP 8-bit floating point, see das_decode_attention_fp8). */
+typedef enum { DAS_F32 = 0, DAS_BF16 = 1, DAS_E4M3 = 2 } das_dtype;
+
+/* Page-pool layouts of a paged K/V cache (see das_decode_attention_paged). */
+typedef enum {
+  DAS_PAGED_HND = 0, /* pool [num_pages][Hkv][page_size][D]: a page's rows of one kv-head contiguous */
+  DAS_PAGED_NHD = 1  /* pool [num_pages][page_size][Hkv][D]: a page's rows, all kv-heads per row */
+} das_paged_layout;
 
 #define DAS_MAX_SPLITS 4096
 /* A workspace begins with this many bytes of arrival counters (see
@@ -189,6 +200,36 @@ int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_ca
                             float scale, void* out, int32_t out_dtype, float* lse_out,
                             int32_t num_splits, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Decode attention over a paged K/V cache ([FD++] §6).  K and V live in two
+ * page pools of num_pages pages of page_size rows; row j of sequence b is
+ * row j % page_size of page block_table[b][j / page_size]:
+ *   k_pool, v_pool  [num_pages][Hkv][page_size][D] (DAS_PAGED_HND) or
+ *                   [num_pages][page_size][Hkv][D] (DAS_PAGED_NHD), elements
+ *                   of kv_dtype: DAS_BF16, or DAS_E4M3 with k_scale/v_scale
+ *                   as in das_decode_attention_fp8 (ignored for DAS_BF16)
+ *   block_table     device int32 [B][max_blocks]; entries of pages a sequence
+ *                   does not reach are never read; an entry outside
+ *                   [0, num_pages) is clamped into it on the device (wrong
+ *                   rows, never an access outside the pool)
+ *   page_size       a power of two, 32 ... 65536 rows (DAS_ENOTSUP otherwise)
+ *   seq_lens[b]     device int32, clamped to [0, max_blocks * page_size]
+ * Splits cover whole pages: the plan is das_plan's for Smax = max_blocks *
+ * page_size with the chunk rounded up to a multiple of page_size, so a
+ * workspace of das_decode_workspace_bytes(B, Hq, Hkv, max_blocks *
+ * page_size, D, num_splits, 0) bytes always suffices.  q, out, lse_out,
+ * num_splits, the workspace precondition, stream, errors: as for
+ * das_decode_attention.  One page's rows of one kv-head are addressed with
+ * 32-bit offsets: page_size * Hkv * D * element bytes < 2^31.
+ */
+int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
+                               int32_t kv_dtype, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, int32_t max_blocks, int32_t page_size,
+                               int32_t num_pages, int32_t layout, const int32_t* seq_lens,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                               void* out, int32_t out_dtype, float* lse_out, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Phase 2 alone ([FD++] §3, phase 2): merges the partial results that

@@ -175,3 +175,42 @@ def test_merge_argument_checks(lib):
     assert f(None, P(16), P(16), P(16), P(16), P(16), 4, 128, 0, None) == das.DAS_EINVAL
     assert f(P(8), P(16), P(16), P(16), P(16), P(16), 4, 128, 0, None) == das.DAS_EINVAL
     assert f(None, None, None, None, None, None, 0, 128, 0, None) == das.DAS_OK  # empty
+
+
+def test_binding_constants_match_the_header():
+    import re
+    text = open(os.path.join(ROOT, "include", "das.h")).read()
+    found = dict(re.findall(r"\b(DAS_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    found.update({k: v for k, v in re.findall(r"#define\s+(DAS_[A-Z0-9_]+)\s+(\d+)\b", text)})
+    assert found, "no constants parsed"
+    for name, value in found.items():
+        assert hasattr(das, name), f"binding lacks {name}"
+        assert getattr(das, name) == int(value), f"{name}: binding {getattr(das, name)} != header {value}"
+
+
+def _call_paged(lib, **kw):
+    a = dict(q=16, k=16, v=16, kvt=das.DAS_BF16, ks=0, vs=0, bt=16, mb=64, P=64, npg=100,
+             lay=das.DAS_PAGED_HND, sl=16, B=1, Hq=8, Hkv=2, D=128, scale=0.1, out=16, dt=0,
+             lse=0, ns=4, ws=16, wsb=1 << 30, st=None)
+    a.update(kw)
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.das_decode_attention_paged(
+        P(a["q"]), P(a["k"]), P(a["v"]), a["kvt"], P(a["ks"]), P(a["vs"]), P(a["bt"]), a["mb"],
+        a["P"], a["npg"], a["lay"], P(a["sl"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+        P(a["out"]), a["dt"], P(a["lse"]), a["ns"], P(a["ws"]), a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=0), das.DAS_EINVAL), (dict(bt=18), das.DAS_EINVAL),        # null / misaligned table
+    (dict(kvt=das.DAS_F32), das.DAS_EINVAL), (dict(kvt=7), das.DAS_EINVAL),
+    (dict(kvt=das.DAS_E4M3), das.DAS_EINVAL),                             # E4M3 without scales
+    (dict(lay=2), das.DAS_EINVAL), (dict(mb=0), das.DAS_EINVAL), (dict(npg=0), das.DAS_EINVAL),
+    (dict(P=16), das.DAS_ENOTSUP), (dict(P=48), das.DAS_ENOTSUP), (dict(P=1 << 17), das.DAS_ENOTSUP),
+    (dict(q=0), das.DAS_EINVAL), (dict(k=8), das.DAS_EINVAL), (dict(D=80), das.DAS_ENOTSUP),
+    (dict(ws=0), das.DAS_EWORKSPACE), (dict(wsb=100), das.DAS_EWORKSPACE),
+    (dict(mb=1 << 26, P=64), das.DAS_EINVAL),                            # max_blocks * P >= 2^31
+    (dict(P=65536, Hq=128, Hkv=128, lay=das.DAS_PAGED_NHD), das.DAS_ENOTSUP),  # page >= 2^31 bytes
+])
+def test_paged_argument_checks(lib, kw, status):
+    # All pointers are fake: a failed check must return before any launch.
+    assert _call_paged(lib, **kw) == status

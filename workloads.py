@@ -294,12 +294,51 @@ PAGED_HND = 0   # pool [num_pages][Hkv][P][D]
 PAGED_NHD = 1   # pool [num_pages][P][Hkv][D]
 
 
+def scatter_to_pages(k: np.ndarray, v: np.ndarray, seq_lens: np.ndarray, page_size: int,
+                     layout: int, seed: int, fill, spare_pages: int = 3):
+    """Cut every sequence's valid rows of k and v ([B][Hkv][Smax][D]) into
+    pages of page_size rows and place the pages in a pool in the order
+    ``PCG64(seed + 7919).permutation``; spare pages (all ``fill``) close the
+    pool and fill the block-table entries past each sequence's last page.
+    Returns (k_pool, v_pool, block_table)."""
+    B, Hkv, S, D = k.shape
+    P = int(page_size)
+    max_blocks = (S + P - 1) // P
+    used = [(int(L) + P - 1) // P for L in seq_lens]
+    n_used = int(sum(used))
+    num_pages = n_used + spare_pages
+    order = np.random.Generator(np.random.PCG64(seed + 7919)).permutation(num_pages)
+    spare = [int(p) for p in order[n_used:]] or [0]
+    table = np.empty((B, max_blocks), dtype=np.int32)
+    shape = (num_pages, Hkv, P, D) if layout == PAGED_HND else (num_pages, P, Hkv, D)
+    k_pool = np.full(shape, fill, dtype=k.dtype)
+    v_pool = np.full(shape, fill, dtype=v.dtype)
+    nxt = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        for i in range(max_blocks):
+            if i < used[b]:
+                page = int(order[nxt])
+                nxt += 1
+                j0, j1 = i * P, min(L, (i + 1) * P)
+                for src, pool in ((k, k_pool), (v, v_pool)):
+                    rows = src[b, :, j0:j1, :]                     # [Hkv][n][D]
+                    if layout == PAGED_HND:
+                        pool[page, :, : j1 - j0, :] = rows
+                    else:
+                        pool[page, : j1 - j0, :, :] = rows.transpose(1, 0, 2)
+                table[b, i] = page
+            else:
+                table[b, i] = spare[i % len(spare)]
+    return k_pool, v_pool, table
+
+
 @dataclasses.dataclass
 class PagedInputs:
-    base: Inputs              # the same rows as a contiguous cache
+    base: object              # Inputs or Fp8Inputs: the same rows as a contiguous cache
     page_size: int
     layout: int
-    k_pool: np.ndarray        # uint16, [num_pages][Hkv][P][D] (HND) or [num_pages][P][Hkv][D] (NHD)
+    k_pool: np.ndarray        # [num_pages][Hkv][P][D] (HND) or [num_pages][P][Hkv][D] (NHD)
     v_pool: np.ndarray
     block_table: np.ndarray   # int32 [B][max_blocks]
 
@@ -310,36 +349,15 @@ class PagedInputs:
 
 def make_paged_inputs(cfg: Config, seed: int, page_size: int, layout: int = PAGED_HND,
                       smax: Optional[int] = None, seq_lens: Optional[Sequence[int]] = None,
-                      spare_pages: int = 3) -> PagedInputs:
-    """``make_inputs`` (same seed, same rows), scattered into a page pool."""
-    base = make_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
-    B, Hkv, S, D = base.k.shape
-    P = int(page_size)
-    max_blocks = (S + P - 1) // P
-    used = [(int(L) + P - 1) // P for L in base.seq_lens]
-    n_used = int(sum(used))
-    num_pages = n_used + spare_pages
-    order = np.random.Generator(np.random.PCG64(seed + 7919)).permutation(num_pages)
-    spare = [int(p) for p in order[n_used:]] or [0]
-    table = np.empty((B, max_blocks), dtype=np.int32)
-    shape = (num_pages, Hkv, P, D) if layout == PAGED_HND else (num_pages, P, Hkv, D)
-    k_pool = np.full(shape, BF16_QNAN, dtype=np.uint16)
-    v_pool = np.full(shape, BF16_QNAN, dtype=np.uint16)
-    nxt = 0
-    for b in range(B):
-        L = int(base.seq_lens[b])
-        for i in range(max_blocks):
-            if i < used[b]:
-                page = int(order[nxt])
-                nxt += 1
-                j0, j1 = i * P, min(L, (i + 1) * P)
-                for src, pool in ((base.k, k_pool), (base.v, v_pool)):
-                    rows = src[b, :, j0:j1, :]                     # [Hkv][n][D]
-                    if layout == PAGED_HND:
-                        pool[page, :, : j1 - j0, :] = rows
-                    else:
-                        pool[page, : j1 - j0, :, :] = rows.transpose(1, 0, 2)
-                table[b, i] = page
-            else:
-                table[b, i] = spare[i % len(spare)]
-    return PagedInputs(base, P, layout, k_pool, v_pool, table)
+                      spare_pages: int = 3, fp8: bool = False) -> PagedInputs:
+    """``make_inputs`` (or ``make_fp8_inputs``; same seed, same rows), scattered
+    into a page pool."""
+    if fp8:
+        base = make_fp8_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        fill = E4M3_NAN
+    else:
+        base = make_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        fill = BF16_QNAN
+    k_pool, v_pool, table = scatter_to_pages(base.k, base.v, base.seq_lens, page_size, layout,
+                                             seed, fill, spare_pages)
+    return PagedInputs(base, int(page_size), layout, k_pool, v_pool, table)
