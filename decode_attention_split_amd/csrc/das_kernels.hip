@@ -14,17 +14,20 @@
 //     byte, so it is bound by HBM bandwidth.  Phase 1 streams K and V with
 //     16-byte loads in which 16 (D=128) or 8 (D=64) consecutive lanes cover
 //     one 256/128-byte row, so each wave-wide load covers whole rows.
-//   * q.K^T for G in {4, 8} is a real (small) matrix product and runs on the
-//     matrix cores: v_mfma_f32_16x16x32_bf16 with the G query heads as rows
-//     and 16 cached rows as columns.  Its B operand wants one row per lane,
-//     which the coalesced load does not give, so each wave stages its K tile
-//     through LDS with an XOR swizzle that keeps both the store and the
-//     column-major read free of bank conflicts.  For G in {1, 2} the product
-//     is a matrix-vector product and runs on the vector ALUs with
-//     v_dot2_f32_bf16 (exact bf16 products, fp32 accumulation).
-//   * p.V runs on the vector ALUs in fp32 straight from the coalesced V
-//     registers; p reaches the lanes that need it through a small per-wave
-//     LDS buffer.
+//   * For G in {4, 8} both products are real (small) matrix products and
+//     run on the matrix cores (v_mfma_f32_16x16x32_bf16).  q.K^T is taken as
+//     K.q^T, 16 cached rows by the G query heads (padded to 16), so that each
+//     lane ends up holding one head's logits for eight rows -- exactly its
+//     slots of the A operand of p.V, with no data movement.  p is split into
+//     two bf16 halves (p = hi + lo to about 2^-18 relative), so p.V keeps
+//     fp32-level accuracy; V is exact in bf16 (and so is E4M3).  K and V go
+//     from HBM straight into a per-wave LDS tile with an XOR swizzle; K is
+//     read one row per lane, V column-wise with the gfx950 transposing LDS
+//     reads (ds_read_b64_tr_b16 / _tr_b8), both free of bank conflicts.
+//   * For G in {1, 2} q.K^T is a matrix-vector product on the vector ALUs
+//     (v_dot2_f32_bf16: exact bf16 products, fp32 accumulation), and p.V runs
+//     on the vector ALUs in fp32 straight from the coalesced V registers; p
+//     reaches the lanes that need it through a small per-wave LDS buffer.
 //   * The online softmax keeps, per wave and head, a running max (base-2
 //     units: logits are scaled by scale*log2(e) in fp32 after the dot) and
 //     rescales the partial sums only when the max grows.
@@ -222,11 +225,43 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Static LDS of split_kv_decode<D, G, kFp8>: per wave a K tile and a p
-// buffer, reused at the end for the wave's state.
+// Static LDS of split_kv_decode<D, G, kFp8>: per wave a K tile and either a
+// V tile (G >= 4: p.V on the matrix cores) or a p buffer (G <= 2), reused at
+// the end for the wave's state.
 template <int D, int G, bool kFp8>
 constexpr int split_smem_bytes() {
-  return kWaves * (kTile * (kFp8 ? 1 : 2) * D + kTile * G * 4);
+  return kWaves * (kTile * (kFp8 ? 1 : 2) * D * (G >= 4 ? 2 : 1) + (G >= 4 ? 0 : kTile * G * 4));
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+// gfx950 transposing LDS reads.  Within each 16-lane group, lane 4q+u (b16)
+// receives as its element e the element u of the 8 bytes addressed by lane
+// 4e+q; lane 8q+u (b8) receives as its byte e the byte u of the 8 bytes
+// addressed by lane 2e+q.  So 16 lanes that address 4 (or 8) rows of a
+// row-major tile, 16 columns at a time, get one column each.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ uint2 lds_read_tr8(const unsigned char* p) {
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// p as the bf16 A operand pair (hi, lo) with hi + lo = p to about 2^-18
+// relative: hi is p rounded to bf16, lo the exact remainder rounded to bf16.
+__device__ __forceinline__ void split_bf16x8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)p[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(p[i] - (float)h);
+  }
 }
 
 constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
@@ -245,9 +280,12 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   constexpr int kElemBytes = kFp8 ? 1 : 2;
   constexpr int kT = kTile;                     // rows per wave per step
   constexpr int kRowBytes = D * kElemBytes;
-  // V: every lane loads 8 elements (16 bytes of bf16, 8 bytes of E4M3) of
-  // one row, D/8 consecutive lanes covering the row; the p.V sums use the
-  // same layout.
+  // G >= 4: p.V on the matrix cores, V staged through LDS like K.
+  constexpr bool kMfmaPv = G >= 4;
+  static_assert(!kMfmaPv || kT == 32, "the p.V operand layout assumes 32-row tiles");
+  // G <= 2, V: every lane loads 8 elements (16 bytes of bf16, 8 bytes of
+  // E4M3) of one row, D/8 consecutive lanes covering the row; the p.V sums
+  // use the same layout.
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kT / kRowsPerLoad;  // V loads per lane per tile
@@ -257,16 +295,19 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   constexpr int kKRowsPerLoad = 64 / kKLanesPerRow;
   constexpr int kKLoads = kT / kKRowsPerLoad;
   constexpr int kKTileBytes = kT * kRowBytes;
-  constexpr int kPBytes = kT * G * 4;
-  constexpr int kWaveBytes = kKTileBytes + kPBytes;
+  constexpr int kVTileBytes = kMfmaPv ? kKTileBytes : 0;
+  constexpr int kPBytes = kMfmaPv ? 0 : kT * G * 4;
+  constexpr int kWaveBytes = kKTileBytes + kVTileBytes + kPBytes;
   constexpr int kSmemBytes = split_smem_bytes<D, G, kFp8>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
+  constexpr int kNBlocks = D / 16;              // p.V MFMA column blocks of 16 dims
   static_assert(kKTileBytes == kKLoads * 1024, "one 1 KiB LDS slab per K load");
   static_assert(kSmemBytes == kWaves * kWaveBytes, "one tile region per wave");
-  // End-of-stream state of a wave: its p.V sums are kept per row group
-  // (lanes with the same row of a load) rather than summed across the wave,
-  // as many row groups as fit in the wave's own tile region.
-  constexpr int kRowGroups = 64 / kLanesPerRow;                     // 4 (D=128) or 8 (D=64)
+  // End-of-stream state of a wave.  G <= 2: the p.V sums are kept per row
+  // group (lanes with the same row of a load) rather than summed across the
+  // wave, as many row groups as fit in the wave's own tile region.  G >= 4:
+  // the matrix cores have already summed over the rows (one group).
+  constexpr int kRowGroups = kMfmaPv ? 1 : 64 / kLanesPerRow;        // 4 (D=128) or 8 (D=64)
   constexpr int kFitGroups = pow2_floor(kWaveBytes / (G * D * 4));
   constexpr int kMergeGroups = kThreads * 4 / (G * D);   // one merging thread per group and quad
   constexpr int kKeptGroups = kRowGroups < kFitGroups
@@ -288,11 +329,11 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int L = clamp_len(a.seq_lens[b], a.Smax);
   // The sequence's rows are cut into chunks of a.chunk rows; split s owns
   // chunk s (chunk * ns >= Smax, so every row has a split).
-  const int nb = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
-  const int nsb = min(a.ns, nb);                // splits this sequence uses
+  const int n_chunks = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
+  const int nsb = min(a.ns, n_chunks);                // splits this sequence uses
   // An empty split exits at once; phase 2 never reads it.  With the fused
   // merge, split 0 of an empty sequence stays to write out = 0, lse = -inf.
-  if (!a.direct && s >= nb && !(a.fused && s == 0)) return;
+  if (!a.direct && s >= n_chunks && !(a.fused && s == 0)) return;
 
   unsigned char* kt = smem + wave * kWaveBytes;
   float* pt = reinterpret_cast<float*>(kt + kKTileBytes);
@@ -325,8 +366,8 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   }
 
   // ---- query operand ----
-  // G >= 4: MFMA A operand; lane i holds head i%16 (zero when >= G) and the
-  //         8 dims of chunk 4*kb + i/16 for k-block kb.
+  // G >= 4: MFMA B operand (q^T); lane i holds head i%16 (zero when >= G)
+  //         and the 8 dims of chunk 4*kb + i/16 for k-block kb.
   // G <= 2: lane i works on row i % kT and the part i / kT of D; it
   //         holds that part of every head as bf16 pairs.
   constexpr int kParts = 64 / kT;
@@ -361,25 +402,34 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     }
   }
 
-  // ---- per-wave running state ----
-  constexpr int kLaneHeads = G >= 4 ? 4 : G;
-  float m_run[G];               // running max per head (base-2 units), wave-uniform
-  float acc[G][8];              // p.V partial sums for this lane's chunk of D
-  float l_lane[kLaneHeads];     // exponential sums of the logits this lane holds
+  // ---- per-wave running state (maxima in base-2 units) ----
+  // G <= 2: wave-uniform running max per head, this lane's exponential sums,
+  //         and p.V sums for this lane's 8 dims of its row.
+  float m_run[G];
+  float acc[G][8];
+  float l_lane[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
+    l_lane[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
+  // G >= 4: lane l keeps the running max and exponential sum of head l%16
+  //         (the four lanes with that head agree on the max) and the p.V sums
+  //         in the MFMA accumulator layout: oacc[nb][r] is head 4*(l/16) + r,
+  //         dim 16*nb + l%16.
+  float m_lane = -INFINITY, l_sum = 0.f;
+  f32x4_t oacc[kNBlocks];
 #pragma unroll
-  for (int i = 0; i < kLaneHeads; ++i) l_lane[i] = 0.f;
+  for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // K goes from HBM straight into the wave's LDS tile (buffer_load ... lds):
   // load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the tile, lane l the
   // 16 bytes at 16*l, i.e. row kKRowsPerLoad*m + k_row_in_load, slot k_slot.
   // The lane fetches the logical chunk whose swizzled slot that is, so the
-  // tile ends up in the k_tile_offset layout.  V goes to registers.
+  // tile ends up in the k_tile_offset layout.  G >= 4: V goes the same way
+  // into the V tile that follows; G <= 2: V goes to registers.
   using VReg = typename std::conditional<kFp8, uint2, uint4>::type;
   // Paged cache: the block-table entry of the page holding row r.  The table
   // is read-only for the whole kernel, so it is read through the constant
@@ -415,12 +465,23 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
           rk, (__attribute__((address_space(3))) void*)(kbuf + m * 1024), 16,
           r * row_stride + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
     }
+    if constexpr (kMfmaPv) {
 #pragma unroll
-    for (int m = 0; m < kLoads; ++m) {
-      if constexpr (kFp8)
-        vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
-      else
-        vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+      for (int m = 0; m < kKLoads; ++m) {
+        const int r = kKRowsPerLoad * m + k_row_in_load;
+        const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(kbuf + kKTileBytes + m * 1024), 16,
+            r * row_stride + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kLoads; ++m) {
+        if constexpr (kFp8)
+          vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+        else
+          vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+      }
     }
   };
 
@@ -436,69 +497,91 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   };
 
   auto process_tile = [&](int r0, const VReg* vr, const unsigned char* ktile) {
-    // the K loads were issued before the V loads: wait for them only
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
-    wave_lds_fence();
-
-    float alpha[G];
-    bool grow = false;
-    if constexpr (G >= 4) {
-      constexpr int kHeadGroups = G / 4;
-      constexpr int kColGroups = kT / 16;
-      const int n = lane & 15;
-      float x[kColGroups][4];
+    if constexpr (kMfmaPv) {
+      // K and V both arrive through LDS
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wave_lds_fence();
+      const unsigned char* vtile = ktile + kKTileBytes;
+      const int n = lane & 15, grp = lane >> 4;
+      // S^T = K q^T: lane l gets the logits of head n for rows 16*tg + 4*grp + r
+      float x[2][4];
 #pragma unroll
-      for (int tg = 0; tg < kColGroups; ++tg) {
+      for (int tg = 0; tg < 2; ++tg) {
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < kKBlocks; ++kb) {
-          const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + (lane >> 4));
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], as_bf16x8(kw), sacc, 0, 0, 0);
+          const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + grp);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
         }
-        const bool ok = r0 + 16 * tg + n < row_end;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[tg][r] = ok ? sacc[r] * c2 : -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          x[tg][r] = (r0 + 16 * tg + 4 * grp + r < row_end) ? sacc[r] * c2 : -INFINITY;
       }
-      // tile max per head: row 16*hg .. 16*hg+15 of the wave holds heads 4*hg + r
-      float mt[4];
+      // tile max of head n over the four lanes that hold it (row r0 is always
+      // valid, so the max is finite)
+      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mt = reduce_lane_bits<4, true>(mt);
+      const float mn = fmaxf(m_lane, mt);
+      const float alpha = fast_exp2(m_lane - mn);
+      const bool grow = __builtin_amdgcn_ballot_w64(mn > m_lane) != 0;
+      m_lane = mn;
+      // p in the A operand's k-slot order: slot i of lane group grp is row
+      // 16*(i/4) + 4*grp + i%4 (the V operand below uses the same order)
+      float pv[8];
+      float lsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mt[r] = x[0][r];
-#pragma unroll
-        for (int tg = 1; tg < kColGroups; ++tg) mt[r] = fmaxf(mt[r], x[tg][r]);
-        mt[r] = row_reduce16<true>(mt[r]);
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = fast_exp2(x[i / 4][i % 4] - mn);
+        lsum += pv[i];
       }
-#pragma unroll
-      for (int hg = 0; hg < kHeadGroups; ++hg) {
+      l_sum = fmaf(l_sum, alpha, lsum);
+      if (grow) {
+        // row r of this lane's accumulators is head 4*grp + r, whose factor
+        // the lane with n = 4*grp + r holds (G = 4: heads 0..3 in group 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int h = 4 * hg + r;
-          const float mn = fmaxf(m_run[h], lane_value(mt[r], 16 * hg));
-          grow |= mn > m_run[h];
-          alpha[h] = fast_exp2(m_run[h] - mn);
-          m_run[h] = mn;
+          float f = lane_value(alpha, r);
+          if constexpr (G == 8) f = grp == 1 ? lane_value(alpha, 4 + r) : f;
+#pragma unroll
+          for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb][r] *= f;
         }
       }
-      const bool upper = kHeadGroups == 2 && lane >= 16;
+      bf16x8_t ph, pl;
+      split_bf16x8(pv, ph, pl);
+      // ---- p.V on the matrix cores: V^T column blocks of 16 dims ----
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ml = upper ? m_run[(4 + r) % G] : m_run[r];
-        const float al = upper ? alpha[(4 + r) % G] : alpha[r];
-        float lsum = 0.f;
-#pragma unroll
-        for (int tg = 0; tg < kColGroups; ++tg) {
-          x[tg][r] = fast_exp2(x[tg][r] - ml);
-          lsum += x[tg][r];
+      for (int nb = 0; nb < kNBlocks; ++nb) {
+        uint4 vw;
+        if constexpr (kFp8) {
+          // lane 8q+u of the group gets byte e from lane 2e+q: lane 2e+q
+          // addresses row 16*(e/4) + 4*grp + e%4, bytes 16*nb + 8q .. +7
+          const int e = n >> 1;
+          const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
+          vw = e4m3x8_to_bf16x8(
+              lds_read_tr8(vtile + k_tile_offset<kRowBytes>(row, nb) + 8 * (lane & 1)));
+        } else {
+          // lane 4q+u of the group gets element e from lane 4e+q: lane 4e+q
+          // addresses row 4*grp + e (+16 for slots 4..7), dims 16*nb + 4q .. +3
+          const int row = 4 * grp + (n >> 2);
+          const int c = 2 * nb + ((lane & 3) >> 1);
+          const uint2 w0 =
+              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row, c) + 8 * (lane & 1));
+          const uint2 w1 =
+              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row + 16, c) + 8 * (lane & 1));
+          vw = make_uint4(w0.x, w0.y, w1.x, w1.y);
         }
-        l_lane[r] = fmaf(l_lane[r], al, lsum);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vw), oacc[nb], 0, 0, 0);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vw), oacc[nb], 0, 0, 0);
       }
-      if (lane < 16 * kHeadGroups) {
-#pragma unroll
-        for (int tg = 0; tg < kColGroups; ++tg)
-          *reinterpret_cast<float4*>(pt + (16 * tg + n) * G + 4 * (lane >> 4)) =
-              make_float4(x[tg][0], x[tg][1], x[tg][2], x[tg][3]);
-      }
+      return;
     } else {
+      // the K loads were issued before the V loads: wait for them only
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+      wave_lds_fence();
+
+      float alpha[G];
+      bool grow = false;
       // lane i: row i % kT, part i / kT of D; then add the parts
       const int n = lane % kT, part = lane / kT;
       float x[G];
@@ -535,48 +618,37 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 #pragma unroll
         for (int h = 0; h < G; ++h) pt[n * G + h] = x[h];
       }
-    }
-    wave_lds_fence();
+      wave_lds_fence();
 
-    // ---- p.V on the vector ALUs ----
-    if (grow) {
+      // ---- p.V on the vector ALUs ----
+      if (grow) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-    }
+          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+      }
 #pragma unroll
-    for (int m = 0; m < kLoads; ++m) {
-      const int r = kRowsPerLoad * m + row_in_load;
-      float ph[G];
-      if constexpr (G >= 4) {
-#pragma unroll
-        for (int h4 = 0; h4 < G / 4; ++h4) {
-          const float4 w = *reinterpret_cast<const float4*>(pt + r * G + 4 * h4);
-          ph[4 * h4 + 0] = w.x;
-          ph[4 * h4 + 1] = w.y;
-          ph[4 * h4 + 2] = w.z;
-          ph[4 * h4 + 3] = w.w;
-        }
-      } else {
+      for (int m = 0; m < kLoads; ++m) {
+        const int r = kRowsPerLoad * m + row_in_load;
+        float ph[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) ph[h] = pt[r * G + h];
-      }
-      float vf[8];
-      if constexpr (kFp8) {
-        e4m3x8_to_f32(vr[m], vf);
-      } else {
-        const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
+        float vf[8];
+        if constexpr (kFp8) {
+          e4m3x8_to_f32(vr[m], vf);
+        } else {
+          const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[2 * i] = bf16_lo(vw[i]);
-          vf[2 * i + 1] = bf16_hi(vw[i]);
+          for (int i = 0; i < 4; ++i) {
+            vf[2 * i] = bf16_lo(vw[i]);
+            vf[2 * i + 1] = bf16_hi(vw[i]);
+          }
         }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[h], vf[e], acc[h][e]);
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[h], vf[e], acc[h][e]);
     }
   };
 
@@ -596,37 +668,41 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   }
 
   // ---- end of the stream: each wave's state into its own tile region ----
-  // acc: lanes lane and lane ^ 2^k for the row-group bits above kKeptGroups
-  // are summed (none for D = 128 with G <= 4); the lanes whose top bits are
-  // zero then hold row group rg = lane / kLanesPerRow.
-  constexpr int kKeepBit = log2_int(kKeptGroups * kLanesPerRow);   // lowest lane bit summed
-  if constexpr (kKeepBit < 6) {
+  // The wave's tiles are no longer needed, and no other wave touches them:
+  // the state goes there without waiting for the others.  Layout [row
+  // group][head][D] floats; max and sum per head in wst_ml.
+  __shared__ float wst_ml[kWaves * 2 * G];
+  float* wst = reinterpret_cast<float*>(kt);
+  if constexpr (kMfmaPv) {
+    l_sum = reduce_lane_bits<4, false>(l_sum);  // lane n: head n's sum over the wave's rows
+    if (lane < 4 * G) {                          // lane groups holding real heads
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int nb = 0; nb < kNBlocks; ++nb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = reduce_lane_bits<kKeepBit, false>(acc[h][e]);
-  }
-  float l_tot[G];
-  if constexpr (G >= 4) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) l_lane[r] = row_reduce16<false>(l_lane[r]);
-#pragma unroll
-    for (int hg = 0; hg < G / 4; ++hg)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) l_tot[4 * hg + r] = lane_value(l_lane[r], 16 * hg);
+        for (int r = 0; r < 4; ++r)
+          wst[(4 * (lane >> 4) + r) * D + 16 * nb + (lane & 15)] = oacc[nb][r];
+    }
+    if (lane < G) {
+      wst_ml[wave * 2 * G + lane] = m_lane;
+      wst_ml[wave * 2 * G + G + lane] = l_sum;
+    }
   } else {
+    // acc: lanes lane and lane ^ 2^k for the row-group bits above kKeptGroups
+    // are summed; the lanes whose top bits are zero then hold row group
+    // rg = lane / kLanesPerRow.
+    constexpr int kKeepBit = log2_int(kKeptGroups * kLanesPerRow);   // lowest lane bit summed
+    if constexpr (kKeepBit < 6) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = reduce_lane_bits<kKeepBit, false>(acc[h][e]);
+    }
+    float l_tot[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float t = row_reduce16<false>(l_lane[h]);
       l_tot[h] = lane_value(t, 0) + (kT == 32 ? lane_value(t, 16) : 0.f);
     }
-  }
-  // The wave's K tile and p buffer are no longer needed, and no other wave
-  // touches them: the state goes there without waiting for the others.
-  // Layout [row group][head][D] floats; max and sum per head in wst_ml.
-  __shared__ float wst_ml[kWaves * 2 * G];
-  {
-    float* wst = reinterpret_cast<float*>(kt);
     if (lane < kKeptGroups * kLanesPerRow) {
       const int rg = lane / kLanesPerRow;
 #pragma unroll
