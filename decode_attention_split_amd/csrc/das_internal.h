@@ -12,14 +12,11 @@ namespace das {
 #ifndef DAS_WAVES
 #define DAS_WAVES 8          // waves per phase-1 workgroup
 #endif
-#ifndef DAS_TILE
-#define DAS_TILE 32          // K/V rows a wave handles per loop iteration (16 or 32)
-#endif
 #ifndef DAS_KV_CACHE_POLICY
 #define DAS_KV_CACHE_POLICY 2  // cache-policy bits of the K/V loads: nt (streamed once)
 #endif
 #ifndef DAS_ONE_PER_CU
-#define DAS_ONE_PER_CU 1     // 1: grids of at most one workgroup per CU are spread one per CU
+#define DAS_ONE_PER_CU 1     // 1: every phase-1 workgroup takes a CU of its own
 #endif
 #ifndef DAS_MIN_WAVES_PER_EU
 #define DAS_MIN_WAVES_PER_EU 2  // waves per SIMD the register allocator must allow
@@ -27,8 +24,7 @@ namespace das {
 
 constexpr int kWaves = DAS_WAVES;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = DAS_TILE;
-static_assert(kTile == 16 || kTile == 32, "tile must be 16 or 32 rows");
+constexpr int kTile = 32;    // K/V rows a wave handles per loop iteration
 
 // Phase 1 (FlashDecoding++ post, §3 phase 1).  One workgroup per
 // (split, kv-head, batch row); it holds every query head of that kv-head.

@@ -118,6 +118,16 @@ __device__ __forceinline__ float reduce_lane_bits(float x) {
 
 constexpr int log2_int(int v) { return v <= 1 ? 0 : 1 + log2_int(v / 2); }
 
+// v from lane K of this lane's 16-lane row (DPP row_newbcast), for K = 0..7
+// into st[0..7].
+template <int K = 0>
+__device__ __forceinline__ void row_broadcast8(float2 v, float2* st) {
+  st[K] = make_float2(
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.x), 0x150 + K, 0xF, 0xF, false)),
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v.y), 0x150 + K, 0xF, 0xF, false)));
+  if constexpr (K + 1 < 8) row_broadcast8<K + 1>(v, st);
+}
+
 // Raw buffer descriptor over `bytes` bytes at `base`: loads past the end
 // return zeros, so a split's rows past its end need no branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   constexpr int kRowBytes = D * kElemBytes;
   // G >= 4: p.V on the matrix cores, V staged through LDS like K.
   constexpr bool kMfmaPv = G >= 4;
-  static_assert(!kMfmaPv || kT == 32, "the p.V operand layout assumes 32-row tiles");
+  static_assert(kT == 32, "the operand layouts assume 32-row tiles");
   // G <= 2, V: every lane loads 8 elements (16 bytes of bf16, 8 bytes of
   // E4M3) of one row, D/8 consecutive lanes covering the row; the p.V sums
   // use the same layout.
@@ -833,6 +843,11 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int h = pair / kQuads, quad = pair % kQuads;
   // This thread's splits, merged online: batches of 8 loaded in one round
   // trip, the running sums rescaled when a batch raises the running max.
+  // The loads are bound by the CU's address rate, so each 16-lane row (one
+  // head, one split group: kGroupLanes is 16 or 32 and divides kQuads) loads
+  // the batch's (max, sum) pairs once, lane x the pair of split x % 8, and
+  // hands them round with row broadcasts.
+  static_assert(kGroupLanes % 16 == 0 && kQuads % kGroupLanes == 0, "one head per row");
   float mt = -INFINITY;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float ls = 0.f;
@@ -840,17 +855,16 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   for (int c0 = grp; c0 < nsb; c0 += kBatch * kGroups) {
     float2 st[kBatch];
     float4 u[kBatch];
+    const int cm = c0 + (lane & 7) * kGroups;
+    const float2 mine =
+        cm < nsb ? coherent_load8(rml, (h * a.ns + cm) * 8) : make_float2(-INFINITY, 0.f);
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int c = c0 + k * kGroups;
-      if (c < nsb) {
-        st[k] = coherent_load8(rml, (h * a.ns + c) * 8);
-        u[k] = coherent_load16(ro, ((h * a.ns + c) * D + 4 * quad) * 4);
-      } else {
-        st[k] = make_float2(-INFINITY, 0.f);
-        u[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      u[k] = c < nsb ? coherent_load16(ro, ((h * a.ns + c) * D + 4 * quad) * 4)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    row_broadcast8(mine, st);
     float bm = st[0].x;
 #pragma unroll
     for (int k = 1; k < kBatch; ++k) bm = fmaxf(bm, st[k].x);
@@ -1058,9 +1072,9 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
 template <int D, int G, bool kFp8, bool kPaged>
 static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipStream_t st) {
   // Dynamic LDS that brings the workgroup's total to kOnePerCuLds, more than
-  // half a CU's LDS, so no second workgroup fits on the CU; a grid with no
-  // more workgroups than CUs then spreads over all of them instead of
-  // doubling up on some.  The static part already counts toward the total.
+  // half a CU's LDS, so no second workgroup fits on the CU and the streaming
+  // workgroups spread over all CUs instead of doubling up on some.  The
+  // static part already counts toward the total.
   constexpr int kStatic = split_smem_bytes<D, G, kFp8>() + kWaves * 2 * G * 4 + 64;
   static_assert(kStatic + 0 <= kMaxLdsPerWorkgroup, "static LDS over the limit");
   constexpr int kPad = kStatic < kOnePerCuLds ? kOnePerCuLds - kStatic : 0;
