@@ -20,6 +20,10 @@ Pieces:
   floating-point K/V cache (FlashDecoding++ post, §4: quantised K/V turned
   back into wider floats inside the kernel), read as OCP E4M3 codes with one
   fp32 scale per kv-head for K and one for V.
+* ``attention_int4`` / ``int4_decode`` -- the same definition over a 4-bit
+  integer K/V cache (same post, §4, which names INT4 beside FP8), read as
+  two's-complement codes, two per byte (element 2i in the low nibble), with
+  one fp32 scale per cached row (batch row, kv-head, token) for K and for V.
 * ``gather_paged`` / ``attention_paged`` -- a paged K/V cache (FlashDecoding++
   post, §6: engines keep K/V in blocks allocated anywhere in a pool, listed
   per sequence by a block table, and map each block onto a slice of a
@@ -105,6 +109,11 @@ class OracleLib:
         lib.das_oracle_attention_fp8.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                                  ctypes.c_double, p, p]
         lib.das_oracle_attention_fp8.restype = None
+        lib.das_oracle_int4_decode.argtypes = [p, ctypes.c_int64, p]
+        lib.das_oracle_int4_decode.restype = None
+        lib.das_oracle_attention_int4.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                                  ctypes.c_double, p, p]
+        lib.das_oracle_attention_int4.restype = None
         lib.das_oracle_max_threads.argtypes = []
         lib.das_oracle_max_threads.restype = ctypes.c_int
         lib.das_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -174,6 +183,40 @@ class OracleLib:
         self.lib.das_oracle_attention_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
                                           _ptr(seq_lens), B, Hq, Hkv, smax, D, float(scale),
                                           _ptr(out), _ptr(lse))
+        return out, lse
+
+    def int4_decode(self, packed) -> np.ndarray:
+        """Values of packed two's-complement INT4 codes (uint8 [..., n/2] ->
+        float64 [..., n]): element 2i is the low nibble of byte i."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.float64)
+        self.lib.das_oracle_int4_decode(_ptr(packed), out.size, _ptr(out))
+        return out
+
+    def attention_int4(self, q, k, v, k_scale, v_scale, seq_lens,
+                       scale: float) -> Tuple[np.ndarray, np.ndarray]:
+        """Unsplit fp64 attention over an INT4 K/V cache: q bf16 bits (uint16),
+        k/v packed INT4 codes (uint8 [B,Hkv,Smax,D/2]), k_scale/v_scale fp32 per
+        cached row [B,Hkv,Smax]."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint8)
+        v = np.ascontiguousarray(v, dtype=np.uint8)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        k_scale = np.ascontiguousarray(k_scale, dtype=np.float32)
+        v_scale = np.ascontiguousarray(v_scale, dtype=np.float32)
+        if q.ndim != 3 or k.ndim != 4 or k.shape != v.shape:
+            raise ValueError("q must be [B,Hq,D]; k and v [B,Hkv,Smax,D/2] of the same shape")
+        B, Hq, D = q.shape
+        Hkv, smax = k.shape[1], k.shape[2]
+        if k.shape[0] != B or 2 * k.shape[3] != D or Hq % Hkv or seq_lens.shape != (B,):
+            raise ValueError("inconsistent shapes")
+        if k_scale.shape != (B, Hkv, smax) or v_scale.shape != (B, Hkv, smax):
+            raise ValueError("k_scale and v_scale must be [B,Hkv,Smax]")
+        out = np.empty((B, Hq, D), dtype=np.float64)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        self.lib.das_oracle_attention_int4(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale),
+                                           _ptr(v_scale), _ptr(seq_lens), B, Hq, Hkv, smax, D,
+                                           float(scale), _ptr(out), _ptr(lse))
         return out, lse
 
     def merge(self, o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
@@ -258,6 +301,14 @@ def attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, la
 
 def e4m3_decode(codes):
     return default().e4m3_decode(codes)
+
+
+def int4_decode(packed):
+    return default().int4_decode(packed)
+
+
+def attention_int4(q, k, v, k_scale, v_scale, seq_lens, scale: float):
+    return default().attention_int4(q, k, v, k_scale, v_scale, seq_lens, scale)
 
 
 def attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale: float):

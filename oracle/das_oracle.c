@@ -311,3 +311,75 @@ void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t
     }
   }
 }
+
+/*
+ * 4-bit integer K/V cache ([FD++] §4 names INT4 beside FP8: quantised K and V
+ * are turned back into wider floats on chip, a quarter of the bf16 bytes).
+ * The pages give neither the code nor the scaling; the readings taken here:
+ * two's-complement 4-bit integers (-8..7), two per byte, element 2i in the
+ * low nibble and element 2i+1 in the high nibble; one fp32 scale per cached
+ * row (batch row, kv-head, token) for K and one for V.  Element d of row j of
+ * kv-head g of batch row b is k_scale[b][g][j] * int4(element d).
+ */
+static int int4_value(uint8_t byte, int high) {
+  const int n = high ? (byte >> 4) : (byte & 15);
+  return n >= 8 ? n - 16 : n;
+}
+
+/* Element i of a packed INT4 array (n elements, n/2 bytes). */
+void das_oracle_int4_decode(const uint8_t* packed, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (double)int4_value(packed[i / 2], (int)(i & 1));
+}
+
+/*
+ * Unsplit attention over an INT4 K/V cache: the same definition as
+ * das_oracle_attention with k = k_scale[b][g][j] * int4(code), v likewise
+ * (exact in double).  k, v: [B][Hkv][Smax][D/2] bytes; k_scale, v_scale:
+ * [B][Hkv][Smax] fp32.
+ */
+void das_oracle_attention_int4(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  const int G = Hq / Hkv;
+  const int row_bytes = D / 2;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / G;
+      const int L = clamp_len(seq_lens[b], Smax);
+      const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
+      const size_t slab = ((size_t)b * Hkv + g) * (size_t)Smax;
+      double* o = out + ((size_t)b * Hq + h) * D;
+      for (int d = 0; d < D; ++d) o[d] = 0.0;
+      if (L == 0) {
+        lse[(size_t)b * Hq + h] = -INFINITY;
+        continue;
+      }
+      double* w = (double*)malloc(sizeof(double) * (size_t)L);
+      double M = -INFINITY;
+      for (int j = 0; j < L; ++j) {
+        const uint8_t* krow = k + (slab + j) * row_bytes;
+        const double ks = (double)k_scale[slab + j];
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+          dot += widen_bf16(qrow[d]) * (ks * (double)int4_value(krow[d / 2], d & 1));
+        w[j] = scale * dot;
+        if (w[j] > M) M = w[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j < L; ++j) {
+        w[j] = exp(w[j] - M);
+        Z += w[j];
+      }
+      for (int j = 0; j < L; ++j) {
+        const uint8_t* vrow = v + (slab + j) * row_bytes;
+        const double vs = (double)v_scale[slab + j];
+        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * (double)int4_value(vrow[d / 2], d & 1));
+      }
+      for (int d = 0; d < D; ++d) o[d] /= Z;
+      lse[(size_t)b * Hq + h] = M + log(Z);
+      free(w);
+    }
+  }
+}

@@ -410,6 +410,91 @@ def pin_fp8_bruteforce_tiny(lib):
         assert abs(l[0, h] - rl) <= 1e-12 * max(1.0, abs(rl)), f"lse head {h}"
 
 
+# ---- 4-bit integer K/V cache: FlashDecoding++ post §4 (INT4 beside FP8) ----
+
+def _small_int4(seed, B=2, Hq=4, Hkv=2, D=16, smax=24, lens=(24, 13), k_mult=1.0):
+    cfg = workloads.custom_config(B, Hq, Hkv, D, smax, k_mult=k_mult)
+    return workloads.make_int4_inputs(cfg, seed, smax=smax, seq_lens=lens)
+
+
+def _int4_by_shifts(packed):
+    """Sign extension by arithmetic shifts of int8 (an independent route):
+    element 2i from the low nibble of byte i, 2i + 1 from the high nibble."""
+    b = np.ascontiguousarray(packed, dtype=np.uint8)
+    lo = ((b << np.uint8(4)).view(np.int8) >> 4).astype(np.float64)
+    hi = (b.view(np.int8) >> 4).astype(np.float64)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.float64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def pin_int4_decode_matches_sign_extension(lib):
+    """All 256 bytes decode as int8 arithmetic shifts sign-extend them."""
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    assert np.array_equal(lib.int4_decode(codes), _int4_by_shifts(codes))
+
+
+def pin_int4_decode_layout(lib):
+    """Bytes whose two elements the format fixes: low nibble first, two's complement."""
+    table = {0x00: (0, 0), 0x01: (1, 0), 0x10: (0, 1), 0x07: (7, 0), 0x08: (-8, 0),
+             0x0F: (-1, 0), 0x70: (0, 7), 0x80: (0, -8), 0xF0: (0, -1), 0x9A: (-6, -7),
+             0x7F: (-1, 7), 0xF7: (7, -1)}
+    codes = np.array([list(table)], dtype=np.uint8)
+    got = lib.int4_decode(codes).reshape(-1, 2)
+    for c, g in zip(table, got):
+        assert tuple(g) == table[c], f"byte 0x{c:02X} -> {tuple(g)}, want {table[c]}"
+
+
+def pin_int4_attention_equals_bf16_definition(lib):
+    """With power-of-two row scales every scale*int4 value is exact in bfloat16,
+    so the 4-bit path must agree bitwise with the (pinned) bf16 definition fed
+    the dequantised values; the scales vary by row, head and batch row."""
+    x = _small_int4(31, Hq=8, Hkv=2, D=32, smax=40, lens=(40, 17))
+    B, Hkv, S = x.k_scale.shape
+    j = np.arange(S)[None, None, :]
+    ks = np.ldexp(1.0, -(1 + (j + np.arange(Hkv)[None, :, None] + 2 * np.arange(B)[:, None, None]) % 4))
+    vs = np.ldexp(1.0, -((3 * j + np.arange(Hkv)[None, :, None] + np.arange(B)[:, None, None]) % 5))
+    ks, vs = ks.astype(np.float32), vs.astype(np.float32)
+    kd = lib.int4_decode(x.k) * ks[..., None]
+    vd = lib.int4_decode(x.v) * vs[..., None]
+    kb, vb = _bits(kd), _bits(vd)
+    assert np.array_equal(_f(kb), kd) and np.array_equal(_f(vb), vd), "dequantised values must be exact in bf16"
+    o4, l4 = lib.attention_int4(x.q, x.k, x.v, ks, vs, x.seq_lens, x.scale)
+    ob, lb = lib.attention(x.q, kb, vb, x.seq_lens, x.scale)
+    assert np.array_equal(o4, ob) and np.array_equal(l4, lb), "int4 vs bf16 definition"
+
+
+def pin_int4_scale_folding(lib):
+    """Doubling every K scale is doubling the softmax scale; doubling every V
+    scale doubles the output and leaves the LSE alone (exact scalings by 2)."""
+    x = _small_int4(33)
+    o, l = lib.attention_int4(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale)
+    o2, l2 = lib.attention_int4(x.q, x.k, x.v, x.k_scale * 2, x.v_scale, x.seq_lens, x.scale)
+    o3, l3 = lib.attention_int4(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale * 2)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3), "k_scale and scale must fold"
+    o4, l4 = lib.attention_int4(x.q, x.k, x.v, x.k_scale, x.v_scale * 2, x.seq_lens, x.scale)
+    assert np.array_equal(o4, 2 * o) and np.array_equal(l4, l), "v_scale must scale the output only"
+    assert not np.allclose(o2, o), "k_scale must matter"
+
+
+def pin_int4_bruteforce_tiny(lib):
+    """The generator's own non-dyadic per-row scales against a pure-Python
+    textbook softmax with math.fsum, the codes decoded by int8 shifts."""
+    x = _small_int4(34, B=2, Hq=4, Hkv=2, D=8, smax=7, lens=(7, 4))
+    o, l = lib.attention_int4(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale)
+    kf, vf, qf = _int4_by_shifts(x.k), _int4_by_shifts(x.v), _f(x.q)
+    for b in range(2):
+        L = int(x.seq_lens[b])
+        for h in range(4):
+            g = h // 2
+            k_rows = [[float(x.k_scale[b, g, j]) * kf[b, g, j, d] for d in range(8)] for j in range(L)]
+            v_rows = [[float(x.v_scale[b, g, j]) * vf[b, g, j, d] for d in range(8)] for j in range(L)]
+            ro, rl = oracle.attention_fsum_textbook(list(qf[b, h]), k_rows, v_rows, x.scale)
+            assert np.allclose(o[b, h], ro, rtol=1e-12, atol=1e-14), f"row {b} head {h}"
+            assert abs(l[b, h] - rl) <= 1e-12 * max(1.0, abs(rl)), f"lse row {b} head {h}"
+
+
 # ---- paged K/V cache: FlashDecoding++ post §6 ----
 
 def pin_paged_gather_inverts_the_generators_scatter(lib):

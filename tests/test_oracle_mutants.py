@@ -44,6 +44,18 @@ MUTANTS = [
     ("fp8_k_scale_dropped", "(ks * e4m3[krow[d]])", "e4m3[krow[d]]"),
     ("fp8_v_scale_from_k", "(vs * e4m3[vrow[d]])", "(ks * e4m3[vrow[d]])"),
     ("fp8_scale_first_head", "const double ks = (double)k_scale[g]", "const double ks = (double)k_scale[0]"),
+    ("int4_unsigned", "return n >= 8 ? n - 16 : n;", "return n;"),
+    ("int4_high_nibble_first", "const int n = high ? (byte >> 4) : (byte & 15);",
+     "const int n = high ? (byte & 15) : (byte >> 4);"),
+    ("int4_sign_off_by_one", "return n >= 8 ? n - 16 : n;", "return n >= 8 ? n - 15 : n;"),
+    ("int4_scale_per_head", "const double ks = (double)k_scale[slab + j];",
+     "const double ks = (double)k_scale[slab];"),
+    ("int4_v_scale_from_k", "const double vs = (double)v_scale[slab + j];",
+     "const double vs = (double)k_scale[slab + j];"),
+    ("int4_v_scale_row_shift", "const double vs = (double)v_scale[slab + j];",
+     "const double vs = (double)v_scale[slab + (j + 1) % L];"),
+    ("int4_byte_index", "dot += widen_bf16(qrow[d]) * (ks * (double)int4_value(krow[d / 2], d & 1));",
+     "dot += widen_bf16(qrow[d]) * (ks * (double)int4_value(krow[d % row_bytes], d & 1));"),
     ("split_chunk_off_by_one", "const int j1 = (j0 + chunk < L) ? j0 + chunk : L;",
      "const int j1 = (j0 + chunk < L) ? j0 + chunk - 1 : L;"),
 ]

@@ -39,3 +39,22 @@ def test_k_multiplier_is_exact():
     b = workloads.make_inputs(cfg4, 3)
     np.testing.assert_array_equal(workloads.bf16_bits_to_f32(b.k), 4 * workloads.bf16_bits_to_f32(a.k))
     assert np.array_equal(a.v, b.v) and np.array_equal(a.q, b.q)
+
+
+def test_int4_generator_codes_scales_and_poison():
+    cfg = workloads.custom_config(2, 4, 2, 32, 40)
+    a = workloads.make_int4_inputs(cfg, 11, seq_lens=(40, 9))
+    b = workloads.make_int4_inputs(cfg, 11, seq_lens=(40, 9))
+    for name in ("q", "k", "v", "k_scale", "v_scale"):
+        assert np.array_equal(getattr(a, name), getattr(b, name), equal_nan=name.endswith("scale"))
+    assert a.k.shape == (2, 2, 40, 16) and a.k_scale.shape == (2, 2, 40)
+    # rows past the valid ones: code byte 0x88 and a NaN scale; valid scales finite and positive
+    assert np.all(a.k[1, :, 9:] == 0x88) and np.all(np.isnan(a.v_scale[1, :, 9:]))
+    assert np.all(a.k_scale[0] > 0) and np.all(np.isfinite(a.k_scale[1, :, :9]))
+    # every nibble value occurs among the valid codes
+    lo = a.k[0] & 15
+    hi = a.k[0] >> 4
+    assert set(np.unique(np.concatenate([lo.ravel(), hi.ravel()]))) == set(range(16))
+    # the same q stream as the bf16 inputs of the same seed
+    assert np.array_equal(a.q, workloads.make_inputs(cfg, 11, seq_lens=(40, 9)).q)
+    assert a.kv_bytes == (40 + 9) * 2 * (16 + 4) * 2

@@ -290,6 +290,90 @@ def config_fp8_inputs(index: int) -> Fp8Inputs:
     return make_fp8_inputs(CONFIGS[index], 42 + index)
 
 
+def _fill_int4_rows(seed: int, tensor: int, B: int, H: int, smax: int, D: int,
+                    lens: np.ndarray, mult: float = 1.0):
+    """Packed INT4 codes and per-row fp32 scales of K (tensor 2) or V (tensor 3).
+
+    Each valid row of standard normals (times ``mult``) gets the scale
+    max|x| / 7.5 and the codes rint(x / scale) clipped to [-8, 7], so every code
+    value occurs; two's-complement nibbles, element 2i in the low nibble.  Rows
+    past the valid ones hold code byte 0x88 and a NaN scale."""
+    codes = np.full((B, H, smax, D // 2), 0x88, dtype=np.uint8)
+    scales = np.full((B, H, smax), np.nan, dtype=np.float32)
+
+    def one(task: int) -> None:
+        b, h = divmod(task, H)
+        L = int(lens[b])
+        if L == 0:
+            return
+        rng = np.random.Generator(np.random.PCG64(seed).jumped(1 + (tensor * B + b) * H + h))
+        x = rng.standard_normal(L * D, dtype=np.float32).reshape(L, D)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        s = (np.max(np.abs(x), axis=1) / np.float32(7.5)).astype(np.float32)
+        s[s == 0] = np.float32(1.0)
+        n = np.clip(np.rint(x / s[:, None]), -8, 7).astype(np.int8).view(np.uint8) & np.uint8(15)
+        codes[b, h, :L, :] = n[:, 0::2] | (n[:, 1::2] << np.uint8(4))
+        scales[b, h, :L] = s
+
+    tasks = range(B * H)
+    workers = min(B * H, max(1, os.cpu_count() or 1), 16)
+    if workers <= 1 or B * H * int(lens.max(initial=0)) * D < (1 << 22):
+        for t in tasks:
+            one(t)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, tasks))
+    return codes, scales
+
+
+@dataclasses.dataclass
+class Int4Inputs:
+    config: Config
+    seed: int
+    q: np.ndarray          # uint16 [B, Hq, D] bf16 bits
+    k: np.ndarray          # uint8 [B, Hkv, Smax, D/2] packed INT4 codes
+    v: np.ndarray          # uint8 [B, Hkv, Smax, D/2] packed INT4 codes
+    k_scale: np.ndarray    # float32 [B, Hkv, Smax]
+    v_scale: np.ndarray    # float32 [B, Hkv, Smax]
+    seq_lens: np.ndarray   # int32 [B]
+    scale: float
+
+    @property
+    def kv_bytes(self) -> int:
+        """Algorithmic bytes: every valid row of K and V read once, D/2 bytes of
+        codes plus its 4-byte scale."""
+        c = self.config
+        return int(self.seq_lens.astype(np.int64).sum()) * c.Hkv * (c.D // 2 + 4) * 2
+
+
+def make_int4_inputs(cfg: Config, seed: int, smax: Optional[int] = None,
+                     seq_lens: Optional[Sequence[int]] = None) -> Int4Inputs:
+    """One seeded input set for ``cfg`` with a 4-bit integer K/V cache (same
+    draw order and streams as the bf16 inputs: seq_lens, q, then K, then V)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+    else:
+        lens = draw_seq_lens(cfg, rng)
+    B = len(lens)
+    S = int(smax if smax is not None else max(cfg.smax, int(lens.max(initial=0))))
+    if lens.size and (lens.min() < 0 or lens.max() > S):
+        raise ValueError("seq_lens must lie in [0, Smax]")
+    if cfg.D % 2:
+        raise ValueError("INT4 rows need an even D")
+    q = f32_to_bf16_bits(rng.standard_normal(B * cfg.Hq * cfg.D, dtype=np.float32))
+    q = q.reshape(B, cfg.Hq, cfg.D)
+    k, ks = _fill_int4_rows(seed, 2, B, cfg.Hkv, S, cfg.D, lens, cfg.k_mult)
+    v, vs = _fill_int4_rows(seed, 3, B, cfg.Hkv, S, cfg.D, lens)
+    return Int4Inputs(cfg, seed, q, k, v, ks, vs, lens, cfg.scale)
+
+
+def config_int4_inputs(index: int) -> Int4Inputs:
+    """The seeded INT4 inputs of workload ``index`` (seed 42 + index)."""
+    return make_int4_inputs(CONFIGS[index], 42 + index)
+
+
 PAGED_HND = 0   # pool [num_pages][Hkv][P][D]
 PAGED_NHD = 1   # pool [num_pages][P][Hkv][D]
 
