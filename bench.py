@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="index into workloads.CONFIGS")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
-    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8", "int4"), default="bf16",
                     help="K/V cache element: bf16, or E4M3 codes with per-kv-head scales")
     ap.add_argument("--paged", type=int, default=0,
                     help="page size in rows: time the paged entry point over a shuffled pool")
@@ -161,12 +161,18 @@ def main():
     das.load_library()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.config]
+    int4 = args.kv_dtype == "int4"
     fp8 = args.kv_dtype == "fp8"
+    quant = fp8 or int4      # codes plus fp32 scales
     paged = None
     if args.paged:
+        if int4:
+            sys.exit("bench.py: there is no paged INT4 cache")
         layout = workloads.PAGED_HND if args.paged_layout == "hnd" else workloads.PAGED_NHD
         paged = workloads.make_paged_inputs(cfg, 42 + args.config, args.paged, layout, fp8=fp8)
         x = paged.base
+    elif int4:
+        x = workloads.config_int4_inputs(args.config)
     else:
         x = workloads.config_fp8_inputs(args.config) if fp8 else workloads.config_inputs(args.config)
     B, Hq, D = x.q.shape
@@ -188,10 +194,13 @@ def main():
     alloc = x.k.nbytes + x.v.nbytes
     copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
     k_scale = v_scale = None
-    if fp8:
+    if quant:
         k_scale, v_scale = torch.from_numpy(x.k_scale).to(dev), torch.from_numpy(x.v_scale).to(dev)
+        if int4:
+            alloc += x.k_scale.nbytes + x.v_scale.nbytes
+            copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
     src_k, src_v = (paged.k_pool, paged.v_pool) if paged is not None else (x.k, x.v)
-    if fp8:
+    if quant:
         k0, v0 = torch.from_numpy(src_k).to(dev), torch.from_numpy(src_v).to(dev)
     else:
         k0, v0 = up(src_k), up(src_v)
@@ -200,9 +209,13 @@ def main():
         copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
         table = torch.from_numpy(paged.block_table).to(dev)
     ks, vs = [k0], [v0]
+    kss, vss = [k_scale], [v_scale]
     for _ in range(copies - 1):
         ks.append(k0.clone())
         vs.append(v0.clone())
+        # an INT4 cache's row scales are streamed with its codes: rotate them too
+        kss.append(k_scale.clone() if int4 else k_scale)
+        vss.append(v_scale.clone() if int4 else v_scale)
     out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
     out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -217,9 +230,10 @@ def main():
                                           paged.layout, out, lse, args.splits, ws,
                                           k_scale=k_scale, v_scale=v_scale)
                  for c in range(copies)]
-    elif fp8:
-        calls = [das.prepare_decode("das_decode_attention_fp8", q, ks[c], vs[c], sl, x.scale, out,
-                                    lse, args.splits, ws, k_scale=k_scale, v_scale=v_scale)
+    elif quant:
+        name = "das_decode_attention_int4" if int4 else "das_decode_attention_fp8"
+        calls = [das.prepare_decode(name, q, ks[c], vs[c], sl, x.scale, out, lse, args.splits, ws,
+                                    k_scale=kss[c], v_scale=vss[c])
                  for c in range(copies)]
     else:
         calls = [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
@@ -257,7 +271,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 K/V, bf16 q" if fp8 else "bf16",
+        "dtype": ("fp8-e4m3 K/V, bf16 q" if fp8 else
+                  "int4 K/V with fp32 row scales, bf16 q" if int4 else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
@@ -281,11 +296,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (fp8 or paged is not None) else measured_traffic(cfg.name, ns),
+            "traffic": None if (quant or paged is not None) else measured_traffic(cfg.name, ns),
             "kernel_us": round(kernel_ms * 1e3, 3),
         },
     }
-    if args.cpu_seconds > 0 and not fp8 and paged is None:
+    if args.cpu_seconds > 0 and not quant and paged is None:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdas.so")
 
 DAS_OK, DAS_EINVAL, DAS_ENOTSUP, DAS_EWORKSPACE, DAS_ELAUNCH = 0, -1, -2, -3, -4
-DAS_F32, DAS_BF16, DAS_E4M3 = 0, 1, 2
+DAS_F32, DAS_BF16, DAS_E4M3, DAS_INT4 = 0, 1, 2, 3
 DAS_PAGED_HND, DAS_PAGED_NHD = 0, 1
 DAS_MAX_SPLITS = 4096
 DAS_CHUNK_QUANTUM = 128
@@ -27,7 +27,7 @@ DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 
 EXPORTED = ("das_plan", "das_decode_workspace_bytes", "das_decode_attention",
             "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
-            "das_decode_attention_paged", "das_lse_combine", "das_merge_attn_states",
+            "das_decode_attention_int4", "das_split_kv_decode_int4", "das_decode_attention_paged", "das_lse_combine", "das_merge_attn_states",
             "das_strerror")
 
 _lib = None
@@ -59,7 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).argtypes = decode_args
         getattr(lib, name).restype = ctypes.c_int
     fp8_args = [p, p, p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_float, p, i32, p, i32, p, sz, p]
-    for name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8"):
+    for name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8",
+                 "das_decode_attention_int4", "das_split_kv_decode_int4"):
         getattr(lib, name).argtypes = fp8_args
         getattr(lib, name).restype = ctypes.c_int
     lib.das_decode_attention_paged.argtypes = [p, p, p, i32, p, p, p, i32, i32, i32, i32, p, i32,
@@ -111,23 +112,27 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _decode_shapes(q, k_cache, v_cache, seq_lens, fp8: bool = False):
+def _decode_shapes(q, k_cache, v_cache, seq_lens, kv_format: int = DAS_BF16):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    kv_dtypes = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
+    kv_dtypes = {DAS_BF16: (torch.bfloat16,), DAS_E4M3: (torch.uint8, torch.float8_e4m3fn),
+                 DAS_INT4: (torch.uint8,)}[kv_format]
     if q.dtype != torch.bfloat16 or k_cache.dtype not in kv_dtypes or v_cache.dtype not in kv_dtypes:
-        raise ValueError("q must be bfloat16; k_cache and v_cache bfloat16, or E4M3 codes "
-                         "(uint8 or float8_e4m3fn) for the fp8 entry points")
+        raise ValueError("q must be bfloat16; k_cache and v_cache bfloat16, E4M3 codes "
+                         "(uint8 or float8_e4m3fn) for the fp8 entry points, or packed INT4 "
+                         "codes (uint8) for the int4 entry points")
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B,Hq,D]; k_cache, v_cache must be [B,Hkv,Smax,D]")
+        raise ValueError("q must be [B,Hq,D]; k_cache, v_cache must be [B,Hkv,Smax,D] "
+                         "([B,Hkv,Smax,D/2] bytes for INT4)")
     B, Hq, D = q.shape
     _, Hkv, Smax, _ = k_cache.shape
-    if k_cache.shape[0] != B or k_cache.shape[3] != D or seq_lens.shape != (B,):
+    row = D // 2 if kv_format == DAS_INT4 else D
+    if k_cache.shape[0] != B or k_cache.shape[3] != row or seq_lens.shape != (B,):
         raise ValueError("shape mismatch between q, caches and seq_lens")
     return B, Hq, Hkv, Smax, D
 
@@ -167,16 +172,28 @@ def _run_decode(fn_name, q, k_cache, v_cache, seq_lens, scale, out, lse_out, out
     return out, lse_out, workspace
 
 
-def _scales(k_scale, v_scale, Hkv):
+def _scales(k_scale, v_scale, shape):
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
-        if not (t.is_cuda and t.is_contiguous()) or t.dtype != torch.float32 or t.shape != (Hkv,):
-            raise ValueError(f"{name} must be a contiguous float32 [Hkv] device tensor")
+        if not (t.is_cuda and t.is_contiguous()) or t.dtype != torch.float32 \
+                or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} device tensor")
+
+
+# the entry points with a quantised cache and the cache format of each
+_SCALED = {"das_decode_attention_fp8": DAS_E4M3, "das_split_kv_decode_fp8": DAS_E4M3,
+           "das_decode_attention_int4": DAS_INT4, "das_split_kv_decode_int4": DAS_INT4}
+
+
+def _scale_shape(kv_format, B, Hkv, Smax):
+    """E4M3: one scale per kv-head; INT4: one per cached row."""
+    return (Hkv,) if kv_format == DAS_E4M3 else (B, Hkv, Smax)
 
 
 def _run_decode_fp8(fn_name, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out,
                     lse_out, out_dtype, num_splits, workspace, stream, with_lse):
-    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fp8=True)
-    _scales(k_scale, v_scale, Hkv)
+    fmt = _SCALED[fn_name]
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fmt)
+    _scales(k_scale, v_scale, _scale_shape(fmt, B, Hkv, Smax))
     out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
     workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
     dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
@@ -212,13 +229,14 @@ def prepare_decode(fn_name: str, q, k_cache, v_cache, seq_lens, scale: float,
                    workspace: torch.Tensor, stream=None, k_scale=None,
                    v_scale=None) -> PreparedCall:
     """Prepared das_decode_attention / das_split_kv_decode call, or their _fp8
-    forms (then with k_scale and v_scale); the same checks run once."""
-    fp8 = fn_name in ("das_decode_attention_fp8", "das_split_kv_decode_fp8")
+    and _int4 forms (then with k_scale and v_scale); the same checks run once."""
+    fmt = _SCALED.get(fn_name, DAS_BF16)
+    fp8 = fmt != DAS_BF16
     if not fp8 and fn_name not in ("das_decode_attention", "das_split_kv_decode"):
         raise ValueError(fn_name)
-    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fp8=fp8)
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fmt)
     if fp8:
-        _scales(k_scale, v_scale, Hkv)
+        _scales(k_scale, v_scale, _scale_shape(fmt, B, Hkv, Smax))
     out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out.dtype, lse_out is not None)
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, num_splits):
@@ -283,6 +301,27 @@ def das_split_kv_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, sca
                            stream, with_lse)
 
 
+def das_decode_attention_int4(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out=None,
+                              lse_out=None, out_dtype=torch.float32, num_splits=0,
+                              workspace=None, stream=None, with_lse=True):
+    """Decode attention over a 4-bit integer K/V cache (packed two's-complement
+    codes uint8 [B,Hkv,Smax,D/2], element 2i in the low nibble; fp32 row scales
+    [B,Hkv,Smax] for K and V); returns (out, lse)."""
+    out, lse_out, _ = _run_decode_fp8("das_decode_attention_int4", q, k_cache, v_cache, k_scale,
+                                      v_scale, seq_lens, scale, out, lse_out, out_dtype,
+                                      num_splits, workspace, stream, with_lse)
+    return out, lse_out
+
+
+def das_split_kv_decode_int4(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, out=None,
+                             lse_out=None, out_dtype=torch.float32, num_splits=0, workspace=None,
+                             stream=None, with_lse=True):
+    """Phase 1 alone over an INT4 K/V cache; returns (out, lse, workspace)."""
+    return _run_decode_fp8("das_split_kv_decode_int4", q, k_cache, v_cache, k_scale, v_scale,
+                           seq_lens, scale, out, lse_out, out_dtype, num_splits, workspace,
+                           stream, with_lse)
+
+
 def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layout, k_scale,
                 v_scale, out, lse_out, out_dtype, num_splits, workspace, stream, with_lse):
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
@@ -313,7 +352,7 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layo
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
     if kv_dtype == DAS_E4M3:
-        _scales(k_scale, v_scale, Hkv)
+        _scales(k_scale, v_scale, (Hkv,))
     max_blocks = block_table.shape[1]
     out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
     workspace, ws_bytes = _workspace(q, B, Hq, Hkv, max_blocks * P, D, num_splits, workspace)

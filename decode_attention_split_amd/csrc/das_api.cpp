@@ -121,26 +121,31 @@ struct Checked {
   int32_t G, ns, chunk;
 };
 
-// Checks shared by every decode entry point.  Nothing is launched on failure.
-// The K/V cache of one call: bf16 rows, or E4M3 codes with fp32 scales per
-// kv-head (FlashDecoding++ post, §4).
+// The K/V cache of one call: bf16 rows, E4M3 codes with fp32 scales per
+// kv-head, or INT4 codes with fp32 scales per cached row (FlashDecoding++
+// post, §4).
 struct KvCache {
   const void* k;
   const void* v;
   const float* k_scale;
   const float* v_scale;
-  bool fp8;
+  int format;                // das::kKvBf16, kKvE4m3 or kKvInt4
   // paged cache (FlashDecoding++ post, §6): k and v are page pools
   const int32_t* block_table = nullptr;
   int32_t max_blocks = 0, page_size = 0, num_pages = 0, layout = 0;
   bool paged() const { return block_table != nullptr; }
-  int elem_bytes() const { return fp8 ? 1 : 2; }
+  // bytes of a row of D elements
+  int64_t row_bytes(int32_t D) const {
+    return format == das::kKvInt4 ? D / 2 : (format == das::kKvE4m3 ? D : 2 * (int64_t)D);
+  }
 };
+
+// Checks shared by every decode entry point.  Nothing is launched on failure.
 
 int check_decode(const void* q, const void* k, const void* v, const int32_t* seq_lens, int32_t B,
                  int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, const void* out,
                  int32_t out_dtype, int32_t num_splits, const void* workspace,
-                 size_t workspace_bytes, bool need_inputs, int elem_bytes, Checked* c,
+                 size_t workspace_bytes, bool need_inputs, int64_t row_bytes, Checked* c,
                  int32_t page_size = 0) {
   if (seq_lens == nullptr || out == nullptr) return DAS_EINVAL;
   if (need_inputs && (q == nullptr || k == nullptr || v == nullptr)) return DAS_EINVAL;
@@ -152,7 +157,7 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   if (!supported_dims(D, G)) return DAS_ENOTSUP;
   // a sequence's K (or V) rows, plus one tile of overhang, are addressed
   // with 32-bit byte offsets
-  if (page_size == 0 && (int64_t)(Smax + 256) * D * elem_bytes > INT32_MAX) return DAS_ENOTSUP;
+  if (page_size == 0 && (int64_t)(Smax + 256) * row_bytes > INT32_MAX) return DAS_ENOTSUP;
   if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
   if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
   int32_t ns = 0, chunk = 0;
@@ -184,7 +189,7 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   a.k_scale = kv.k_scale;
   a.v_scale = kv.v_scale;
   if (kv.paged()) {
-    const int E = kv.elem_bytes();
+    const int E = (int)kv.row_bytes(D) / D;   // bf16 or E4M3 pools
     int shift = 0;
     while ((1 << shift) < kv.page_size) ++shift;
     a.block_table = kv.block_table;
@@ -224,7 +229,7 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   // once (the ragged G=8 batch on an E4M3 cache: 103 us doubled up, 73 us
   // spread).
   const bool one_per_cu = DAS_ONE_PER_CU != 0;
-  return das::launch_split_kv_decode(D, c.G, kv.fp8, kv.paged(), B, a, one_per_cu, st) ==
+  return das::launch_split_kv_decode(D, c.G, kv.format, kv.paged(), B, a, one_per_cu, st) ==
                  hipSuccess
              ? DAS_OK
              : DAS_ELAUNCH;
@@ -255,7 +260,7 @@ int split_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
                void* stream) {
   Checked c{};
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
-                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c);
+                              num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c);
   if (rc != DAS_OK) return rc;
   return run_phase1(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                     workspace, c, false, static_cast<hipStream_t>(stream));
@@ -267,7 +272,7 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
                 void* stream) {
   Checked c{};
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
-                              num_splits, workspace, workspace_bytes, true, kv.elem_bytes(), &c,
+                              num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c,
                               kv.page_size);
   if (rc != DAS_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -312,7 +317,7 @@ int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
                         int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
                         float* lse_out, int32_t num_splits, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  const KvCache kv{k_cache, v_cache, nullptr, nullptr, false};
+  const KvCache kv{k_cache, v_cache, nullptr, nullptr, das::kKvBf16};
   return split_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                     num_splits, workspace, workspace_bytes, stream);
 }
@@ -324,7 +329,20 @@ int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_ca
                             int32_t num_splits, void* workspace, size_t workspace_bytes,
                             void* stream) {
   if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
-  const KvCache kv{k_cache, v_cache, k_scale, v_scale, true};
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, das::kKvE4m3};
+  return split_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                    num_splits, workspace, workspace_bytes, stream);
+}
+
+int das_split_kv_decode_int4(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                             float scale, void* out, int32_t out_dtype, float* lse_out,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
+  if (((uintptr_t)k_scale & 3u) != 0 || ((uintptr_t)v_scale & 3u) != 0) return DAS_EINVAL;
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, das::kKvInt4};
   return split_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                     num_splits, workspace, workspace_bytes, stream);
 }
@@ -335,7 +353,7 @@ int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                     void* stream) {
   Checked c{};
   const int rc = check_decode(nullptr, nullptr, nullptr, seq_lens, B, Hq, Hkv, Smax, D, 1.0f, out,
-                              out_dtype, num_splits, workspace, workspace_bytes, false, 1, &c);
+                              out_dtype, num_splits, workspace, workspace_bytes, false, D, &c);
   if (rc != DAS_OK) return rc;
   return run_phase2(seq_lens, B, Hq, Smax, D, workspace, out, out_dtype, lse_out, c,
                     static_cast<hipStream_t>(stream));
@@ -346,7 +364,7 @@ int das_decode_attention(const void* q, const void* k_cache, const void* v_cache
                          int32_t Smax, int32_t D, float scale, void* out, int32_t out_dtype,
                          float* lse_out, int32_t num_splits, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  const KvCache kv{k_cache, v_cache, nullptr, nullptr, false};
+  const KvCache kv{k_cache, v_cache, nullptr, nullptr, das::kKvBf16};
   return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                      num_splits, workspace, workspace_bytes, stream);
 }
@@ -358,7 +376,20 @@ int das_decode_attention_fp8(const void* q, const void* k_cache, const void* v_c
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream) {
   if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
-  const KvCache kv{k_cache, v_cache, k_scale, v_scale, true};
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, das::kKvE4m3};
+  return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
+                     num_splits, workspace, workspace_bytes, stream);
+}
+
+int das_decode_attention_int4(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                              float scale, void* out, int32_t out_dtype, float* lse_out,
+                              int32_t num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (k_scale == nullptr || v_scale == nullptr) return DAS_EINVAL;
+  if (((uintptr_t)k_scale & 3u) != 0 || ((uintptr_t)v_scale & 3u) != 0) return DAS_EINVAL;
+  const KvCache kv{k_cache, v_cache, k_scale, v_scale, das::kKvInt4};
   return decode_impl(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                      num_splits, workspace, workspace_bytes, stream);
 }
@@ -370,6 +401,7 @@ int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_
                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                                void* out, int32_t out_dtype, float* lse_out, int32_t num_splits,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_dtype == DAS_INT4) return DAS_ENOTSUP;   // INT4 caches are contiguous
   if (kv_dtype != DAS_BF16 && kv_dtype != DAS_E4M3) return DAS_EINVAL;
   const bool fp8 = kv_dtype == DAS_E4M3;
   if (fp8 && (k_scale == nullptr || v_scale == nullptr)) return DAS_EINVAL;
@@ -382,7 +414,8 @@ int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_
   // one page's rows of one kv-head are addressed with 32-bit byte offsets
   const int64_t E = fp8 ? 1 : 2;
   if ((int64_t)page_size * Hkv * D * E > INT32_MAX) return DAS_ENOTSUP;
-  KvCache kv{k_pool, v_pool, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr, fp8};
+  KvCache kv{k_pool, v_pool, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
+             fp8 ? das::kKvE4m3 : das::kKvBf16};
   kv.block_table = block_table;
   kv.max_blocks = max_blocks;
   kv.page_size = page_size;

@@ -26,13 +26,20 @@ constexpr int kWaves = DAS_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;    // K/V rows a wave handles per loop iteration
 
+// K/V cache element formats (FlashDecoding++ post, §4: quantised caches are
+// turned back into wider floats on chip).
+constexpr int kKvBf16 = 0;   // bf16 rows of D elements
+constexpr int kKvE4m3 = 1;   // E4M3 codes, one fp32 scale per kv-head for K and for V
+constexpr int kKvInt4 = 2;   // two's-complement 4-bit codes, two per byte (low nibble
+                             // first), one fp32 scale per cached row for K and for V
+
 // Phase 1 (FlashDecoding++ post, §3 phase 1).  One workgroup per
 // (split, kv-head, batch row); it holds every query head of that kv-head.
 struct SplitArgs {
   const uint16_t* q;         // bf16 [B][Hq][D]
-  const void* k;             // [B][Hkv][Smax][D] bf16, or E4M3 codes
-  const void* v;             // [B][Hkv][Smax][D] bf16, or E4M3 codes
-  const float* k_scale;      // E4M3 cache: fp32 [Hkv] (FlashDecoding++ post, §4); else unused
+  const void* k;             // [B][Hkv][Smax][D] bf16 or E4M3 codes, [..][D/2] INT4 bytes
+  const void* v;
+  const float* k_scale;      // E4M3: fp32 [Hkv]; INT4: fp32 [B][Hkv][Smax]; bf16: unused
   const float* v_scale;
   const int32_t* seq_lens;   // int32 [B]
   int32_t Hq, Hkv, Smax;
@@ -90,7 +97,7 @@ struct MergeArgs {
 // a second one on its CU.
 constexpr int kMaxLdsPerWorkgroup = 160 * 1024;
 constexpr int kOnePerCuLds = 84 * 1024;
-hipError_t launch_split_kv_decode(int D, int G, bool fp8, bool paged, int B, const SplitArgs& a,
+hipError_t launch_split_kv_decode(int D, int G, int kv_format, bool paged, int B, const SplitArgs& a,
                                   bool one_per_cu, hipStream_t stream);
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t stream);
 hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t stream);

@@ -151,13 +151,14 @@ __device__ __forceinline__ int k_tile_offset(int r, int c) {
   return r * kRowBytes + ((c ^ ((r / kRowsPerBank) % kChunks)) << 4);
 }
 
-// Eight E4M3 codes (OCP 8-bit floating point) as eight bf16 values; the
-// conversion is exact (4 significant bits, a subset of bf16's range).
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w) {
-  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
-  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
-  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
-  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+// Eight E4M3 codes (OCP 8-bit floating point) as eight bf16 values, times
+// the power of two `scale`; the conversion is exact (4 significant bits, a
+// subset of bf16's range).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 w, float scale = 1.0f) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, scale, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, scale, true);
   return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
                     __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
@@ -170,6 +171,43 @@ __device__ __forceinline__ void e4m3x8_to_f32(uint2 w, float* f) {
   const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(w.y, true);
   f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+// INT4 codes through the E4M3 converters: a two's-complement nibble n with
+// its top bit flipped is u = n + 8 in 0..15, and the byte u read as an E4M3
+// code is u * 2^-9 exactly (u < 8: subnormal m = u; u >= 8: exponent 1,
+// mantissa u - 8).  So the converters give u exactly, and the fixed offset 8
+// is taken off by the caller (by linearity, once per dot product or sum).
+// The eight codes of one dword w (elements 0..7, element 2i in the low
+// nibble of byte i), as bf16 values u in the order 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ uint4 int4x8_to_bf16x8_offset8(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  return e4m3x8_to_bf16x8(make_uint2(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu), 512.0f);
+}
+
+// The eight codes of one dword as fp32 n * 2^-9, in element order (exact:
+// u * 2^-9 from the converter minus 8 * 2^-9).
+__device__ __forceinline__ void int4x8_to_f32_scaled(uint32_t w, float* f) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  constexpr float kOff = 8.0f / 512.0f;
+  f[0] = a[0] - kOff; f[2] = a[1] - kOff; f[4] = b[0] - kOff; f[6] = b[1] - kOff;
+  f[1] = c[0] - kOff; f[3] = c[1] - kOff; f[5] = d[0] - kOff; f[7] = d[1] - kOff;
+}
+
+// Eight bf16 (a uint4, element 2i in the low half of word i) reordered to
+// 0, 2, 4, 6, 1, 3, 5, 7: the order int4x8_to_bf16x8_offset8 gives codes in.
+__device__ __forceinline__ uint4 bf16x8_even_odd(uint4 w) {
+  return make_uint4((w.x & 0xFFFFu) | (w.y << 16), (w.z & 0xFFFFu) | (w.w << 16),
+                    (w.x >> 16) | (w.y & 0xFFFF0000u), (w.z >> 16) | (w.w & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, DAS_KV_CACHE_POLICY);
 }
 
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -235,12 +273,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Static LDS of split_kv_decode<D, G, kFp8>: per wave a K tile and either a
-// V tile (G >= 4: p.V on the matrix cores) or a p buffer (G <= 2), reused at
-// the end for the wave's state.
-template <int D, int G, bool kFp8>
+// Bytes of one cached row of D elements.
+template <int D, int kKv>
+constexpr int kv_row_bytes() { return kKv == kKvInt4 ? D / 2 : (kKv == kKvE4m3 ? D : 2 * D); }
+
+// Static LDS of split_kv_decode<D, G, kKv>: per wave a K tile and either a
+// V tile (G >= 4: p.V on the matrix cores; an INT4 cache adds the tile's row
+// scales) or a p buffer (G <= 2), reused at the end for the wave's state.
+template <int D, int G, int kKv>
 constexpr int split_smem_bytes() {
-  return kWaves * (kTile * (kFp8 ? 1 : 2) * D * (G >= 4 ? 2 : 1) + (G >= 4 ? 0 : kTile * G * 4));
+  return kWaves * (kTile * kv_row_bytes<D, kKv>() * (G >= 4 ? 2 : 1) +
+                   (G >= 4 ? (kKv == kKvInt4 ? 2 * kTile * 4 : 0) : kTile * G * 4));
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -278,37 +321,43 @@ constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
 
 // ---------------------------------------------------------------------------
 // Phase 1: split_kv_decode.  Grid (ns | 1, Hkv, B), kThreads threads.
-// kFp8: K and V are E4M3 codes with one fp32 scale per kv-head each
-// (FlashDecoding++ post, §4), dequantised on chip; otherwise bf16.
+// kKv: bf16 rows, E4M3 codes with one fp32 scale per kv-head each, or INT4
+// codes with one fp32 scale per cached row each (FlashDecoding++ post, §4:
+// dequantised on chip, right after the load).
 // kPaged: K and V live in page pools listed by a block table (same post,
 // §6); a tile never straddles a page (pages are >= 32 rows, chunks whole
 // pages), so every tile finds its page with one table entry.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool kFp8, bool kPaged>
+template <int D, int G, int kKv, bool kPaged>
 __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     void split_kv_decode_kernel(SplitArgs a) {
-  constexpr int kElemBytes = kFp8 ? 1 : 2;
+  constexpr bool kFp8 = kKv == kKvE4m3;
+  constexpr bool kInt4 = kKv == kKvInt4;
+  static_assert(!(kInt4 && kPaged), "INT4 caches are contiguous");
   constexpr int kT = kTile;                     // rows per wave per step
-  constexpr int kRowBytes = D * kElemBytes;
+  constexpr int kRowBytes = kv_row_bytes<D, kKv>();
   // G >= 4: p.V on the matrix cores, V staged through LDS like K.
   constexpr bool kMfmaPv = G >= 4;
   static_assert(kT == 32, "the operand layouts assume 32-row tiles");
-  // G <= 2, V: every lane loads 8 elements (16 bytes of bf16, 8 bytes of
-  // E4M3) of one row, D/8 consecutive lanes covering the row; the p.V sums
-  // use the same layout.
+  // G <= 2, V: every lane loads 8 elements (16 bytes of bf16, 8 of E4M3, 4
+  // of INT4) of one row, D/8 consecutive lanes covering the row; the p.V
+  // sums use the same layout.
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kT / kRowsPerLoad;  // V loads per lane per tile
-  constexpr int kVLaneBytes = 8 * kElemBytes;
+  constexpr int kVLaneBytes = kRowBytes / kLanesPerRow;
   // K: 16-byte loads straight into LDS, kKLanesPerRow lanes per row.
   constexpr int kKLanesPerRow = kRowBytes / 16;
   constexpr int kKRowsPerLoad = 64 / kKLanesPerRow;
   constexpr int kKLoads = kT / kKRowsPerLoad;
   constexpr int kKTileBytes = kT * kRowBytes;
   constexpr int kVTileBytes = kMfmaPv ? kKTileBytes : 0;
+  // INT4 on the matrix-core path: the tile's K row scales, then its V row
+  // scales, one float per row
+  constexpr int kScaleBytes = (kMfmaPv && kInt4) ? 2 * kT * 4 : 0;
   constexpr int kPBytes = kMfmaPv ? 0 : kT * G * 4;
-  constexpr int kWaveBytes = kKTileBytes + kVTileBytes + kPBytes;
-  constexpr int kSmemBytes = split_smem_bytes<D, G, kFp8>();
+  constexpr int kWaveBytes = kKTileBytes + kVTileBytes + kScaleBytes + kPBytes;
+  constexpr int kSmemBytes = split_smem_bytes<D, G, kKv>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
   constexpr int kNBlocks = D / 16;              // p.V MFMA column blocks of 16 dims
   static_assert(kKTileBytes == kKLoads * 1024, "one 1 KiB LDS slab per K load");
@@ -346,7 +395,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   if (!a.direct && s >= n_chunks && !(a.fused && s == 0)) return;
 
   unsigned char* kt = smem + wave * kWaveBytes;
-  float* pt = reinterpret_cast<float*>(kt + kKTileBytes);
+  float* pt = reinterpret_cast<float*>(kt + kKTileBytes);   // G <= 2
 
   // The sequence's valid rows of K and V as bounds-checked buffers: loads
   // past row L return zeros, and the rows beyond seq_lens are never read.
@@ -360,6 +409,11 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + slab, kPaged ? 0 : L * kRowBytes);
   const __amdgpu_buffer_rsrc_t rv_seq =
       make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + slab, kPaged ? 0 : L * kRowBytes);
+  // INT4: the sequence's row scales of K and V, L floats each (rows past the
+  // sequence read as 0, checked per row)
+  const size_t scale_slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax;
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + (kInt4 ? scale_slab : 0), kInt4 ? L * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + (kInt4 ? scale_slab : 0), kInt4 ? L * 4 : 0);
   int row_end = 0;                              // end of the chunk being streamed
   const int row_in_load = lane / kLanesPerRow;  // this lane's V row within a load
   const int chunk = lane % kLanesPerRow;        // this lane's 8 elements of a V row
@@ -367,7 +421,8 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int k_row_in_load = lane / kKLanesPerRow;
   const int k_slot = lane % kKLanesPerRow;
   // Logits in base-2 units; an E4M3 cache's K scale multiplies the finished
-  // dot product, its V scale the finished p.V sums.
+  // dot product, its V scale the finished p.V sums.  An INT4 cache's row
+  // scales multiply each row's dot product and each row's p.
   float c2 = a.scale_log2e;
   float v_scale = 1.f;
   if constexpr (kFp8) {
@@ -377,38 +432,60 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   // ---- query operand ----
   // G >= 4: MFMA B operand (q^T); lane i holds head i%16 (zero when >= G)
-  //         and the 8 dims of chunk 4*kb + i/16 for k-block kb.
+  //         and, for k-block kb, the 8 dims of chunk 4*kb + i/16 (INT4:
+  //         chunk (i/16)*kKBlocks + kb, the lane's K bytes being contiguous).
   // G <= 2: lane i works on row i % kT and the part i / kT of D; it
   //         holds that part of every head as bf16 pairs.
+  // INT4 codes convert in the order 0, 2, 4, 6, 1, 3, 5, 7 within each
+  // group of 8 dims, so q's dims are held in that order too, and the sum of
+  // q over D is kept to take off the codes' offset: (q.(u - 8)) = q.u - 8 sum(q).
   constexpr int kParts = 64 / kT;
   constexpr int kPartDims = D / kParts;
   bf16x8_t qa[kKBlocks];
   uint32_t qv[G <= 2 ? G : 1][G <= 2 ? kPartDims / 2 : 1];
+  float q8[G <= 2 ? G : 1];     // INT4: 8 * sum(q) per head (G >= 4: the lane's head)
+  auto bf16x8_sum = [](uint4 w) {
+    return ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
+           ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
+  };
   if constexpr (G >= 4) {
     const int hh = lane & 15;
+    float qs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kKBlocks; ++kb) {
       uint4 w = make_uint4(0, 0, 0, 0);
       if (hh < G) {
         const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + hh) * D;
-        w = *reinterpret_cast<const uint4*>(qrow + 8 * (4 * kb + (lane >> 4)));
+        const int c = kInt4 ? (lane >> 4) * kKBlocks + kb : 4 * kb + (lane >> 4);
+        w = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+      }
+      if constexpr (kInt4) {
+        qs += bf16x8_sum(w);
+        w = bf16x8_even_odd(w);
       }
       qa[kb] = as_bf16x8(w);
     }
+    if constexpr (kInt4) q8[0] = 8.f * reduce_lane_bits<4, false>(qs);
   } else {
     const int part = lane / kT;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const uint4* qrow = reinterpret_cast<const uint4*>(
           a.q + ((size_t)b * a.Hq + (size_t)g * G + h) * D + part * kPartDims);
+      float qs = 0.f;
 #pragma unroll
       for (int i = 0; i < kPartDims / 8; ++i) {
-        const uint4 w = qrow[i];
+        uint4 w = qrow[i];
+        if constexpr (kInt4) {
+          qs += bf16x8_sum(w);
+          w = bf16x8_even_odd(w);
+        }
         qv[h][4 * i + 0] = w.x;
         qv[h][4 * i + 1] = w.y;
         qv[h][4 * i + 2] = w.z;
         qv[h][4 * i + 3] = w.w;
       }
+      if constexpr (kInt4) q8[h] = 8.f * reduce_lane_bits<log2_int(kT), false>(qs);
     }
   }
 
@@ -429,10 +506,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   //         (the four lanes with that head agree on the max) and the p.V sums
   //         in the MFMA accumulator layout: oacc[nb][r] is head 4*(l/16) + r,
   //         dim 16*nb + l%16.
+  //         INT4: oacc[2*cb + h][r] is dim 32*cb + 16*(l%16 / 8) + 2*(l%8) + h,
+  //         and osum[r] the sum of head 4*(l/16) + r's p (times the row
+  //         scales) that the offset of the codes multiplies.
   float m_lane = -INFINITY, l_sum = 0.f;
   f32x4_t oacc[kNBlocks];
 #pragma unroll
   for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t osum = {0.f, 0.f, 0.f, 0.f};
 
   // K goes from HBM straight into the wave's LDS tile (buffer_load ... lds):
   // load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the tile, lane l the
@@ -440,7 +521,10 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   // The lane fetches the logical chunk whose swizzled slot that is, so the
   // tile ends up in the k_tile_offset layout.  G >= 4: V goes the same way
   // into the V tile that follows; G <= 2: V goes to registers.
-  using VReg = typename std::conditional<kFp8, uint2, uint4>::type;
+  using VReg = typename std::conditional<
+      kInt4, uint32_t, typename std::conditional<kFp8, uint2, uint4>::type>::type;
+  // INT4, G <= 2: the K and V scales of this lane's row (lane % kT) of the tile
+  float row_ks = 0.f, row_vs = 0.f;
   // Paged cache: the block-table entry of the page holding row r.  The table
   // is read-only for the whole kernel, so it is read through the constant
   // address space, which makes this a scalar load that only its use waits
@@ -454,6 +538,20 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf, int page) {
     __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
     int soff = r0 * kRowBytes;
+    if constexpr (kInt4) {
+      // row scales first, so that waiting for K also covers them
+      if constexpr (kMfmaPv) {
+        // one dword per row into the scale area: lanes 0..31 K, 32..63 V
+        auto* sdst = (__attribute__((address_space(3))) void*)(kbuf + 2 * kKTileBytes);
+        if (lane < kT)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, sdst, 4, lane * 4, r0 * 4, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, sdst, 4, (lane - kT) * 4, r0 * 4, 0, 0);
+      } else {
+        row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (lane % kT) * 4, r0 * 4, 0));
+        row_vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane % kT) * 4, r0 * 4, 0));
+      }
+    }
     if constexpr (kPaged) {
       // this tile's page; a table entry outside the pool is clamped into it
       // (wrong rows, never an access outside the pool)
@@ -487,7 +585,9 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     } else {
 #pragma unroll
       for (int m = 0; m < kLoads; ++m) {
-        if constexpr (kFp8)
+        if constexpr (kInt4)
+          vr[m] = buffer_load4(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+        else if constexpr (kFp8)
           vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
         else
           vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
@@ -495,9 +595,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     }
   };
 
-  // Elements 8*grp8 .. 8*grp8+7 of row r of a K tile, as bf16.
+  // Elements 8*grp8 .. 8*grp8+7 of row r of a K tile, as bf16 (INT4: the
+  // offset codes u, in the order 0, 2, 4, 6, 1, 3, 5, 7).
   auto k_group = [&](const unsigned char* ktile, int r, int grp8) -> uint4 {
-    if constexpr (kFp8) {
+    if constexpr (kInt4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          ktile + k_tile_offset<kRowBytes>(r, grp8 >> 2) + 4 * (grp8 & 3));
+      return int4x8_to_bf16x8_offset8(w);
+    } else if constexpr (kFp8) {
       const uint2 w = *reinterpret_cast<const uint2*>(
           ktile + k_tile_offset<kRowBytes>(r, grp8 >> 1) + 8 * (grp8 & 1));
       return e4m3x8_to_bf16x8(w);
@@ -513,15 +618,44 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       wave_lds_fence();
       const unsigned char* vtile = ktile + kKTileBytes;
       const int n = lane & 15, grp = lane >> 4;
+      // INT4: the tile's row scales (K at [0, kT), V at [kT, 2 kT))
+      const float* sct = reinterpret_cast<const float*>(ktile + 2 * kKTileBytes);
       // S^T = K q^T: lane l gets the logits of head n for rows 16*tg + 4*grp + r
       float x[2][4];
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kInt4) {
+          // the lane's kKBlocks * 4 contiguous bytes of row 16*tg + n: one
+          // dword (8 codes) per k-block
+          constexpr int kLaneBytes = kKBlocks * 4;
+          const unsigned char* kp = ktile +
+                                    k_tile_offset<kRowBytes>(16 * tg + n, (grp * kLaneBytes) >> 4) +
+                                    ((grp * kLaneBytes) & 15);
+          uint32_t kw[kKBlocks];
+          if constexpr (kKBlocks == 4) {
+            const uint4 t = *reinterpret_cast<const uint4*>(kp);
+            kw[0] = t.x; kw[1] = t.y; kw[2] = t.z; kw[3] = t.w;
+          } else {
+            const uint2 t = *reinterpret_cast<const uint2*>(kp);
+            kw[0] = t.x; kw[1] = t.y;
+          }
 #pragma unroll
-        for (int kb = 0; kb < kKBlocks; ++kb) {
-          const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + grp);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
+          for (int kb = 0; kb < kKBlocks; ++kb)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(int4x8_to_bf16x8_offset8(kw[kb])), qa[kb], sacc, 0, 0, 0);
+          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale
+          const float4 ks = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
+          sacc[0] = (sacc[0] - q8[0]) * ks.x;
+          sacc[1] = (sacc[1] - q8[0]) * ks.y;
+          sacc[2] = (sacc[2] - q8[0]) * ks.z;
+          sacc[3] = (sacc[3] - q8[0]) * ks.w;
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < kKBlocks; ++kb) {
+            const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + grp);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -555,11 +689,49 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
           if constexpr (G == 8) f = grp == 1 ? lane_value(alpha, 4 + r) : f;
 #pragma unroll
           for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb][r] *= f;
+          if constexpr (kInt4) osum[r] *= f;
         }
+      }
+      if constexpr (kInt4) {
+        // p times the row's V scale (rows past the sequence have scale 0 and p 0)
+        const float4 v0 = *reinterpret_cast<const float4*>(sct + kT + 4 * grp);
+        const float4 v1 = *reinterpret_cast<const float4*>(sct + kT + 16 + 4 * grp);
+        pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
+        pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
       }
       bf16x8_t ph, pl;
       split_bf16x8(pv, ph, pl);
-      // ---- p.V on the matrix cores: V^T column blocks of 16 dims ----
+      // ---- p.V on the matrix cores ----
+      if constexpr (kInt4) {
+        // V^T column blocks of 32 dims: lane 8q+u of the group gets byte e
+        // from lane 2e+q, which addresses row 16*(e/4) + 4*grp + e%4, bytes
+        // 16*cb + 8q .. +7; so byte e holds row e's dims 32*cb + 16q + 2u
+        // (low nibble) and + 1 (high nibble): one column of each of two
+        // MFMAs.  The offset 8 of the codes comes off at the end through
+        // osum, the same products against a column of ones.
+        const int e = n >> 1;
+        const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) {
+          const uint2 w =
+              lds_read_tr8(vtile + k_tile_offset<kRowBytes>(row, cb) + 8 * (lane & 1));
+          const uint32_t x0 = w.x ^ 0x88888888u, x1 = w.y ^ 0x88888888u;
+          const uint4 vlo = e4m3x8_to_bf16x8(make_uint2(x0 & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu), 512.0f);
+          const uint4 vhi = e4m3x8_to_bf16x8(
+              make_uint2((x0 >> 4) & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu), 512.0f);
+          oacc[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vlo), oacc[2 * cb], 0, 0, 0);
+          oacc[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vlo), oacc[2 * cb], 0, 0, 0);
+          oacc[2 * cb + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vhi), oacc[2 * cb + 1], 0, 0, 0);
+          oacc[2 * cb + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vhi), oacc[2 * cb + 1], 0, 0, 0);
+        }
+        const uint4 one4 = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        osum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(one4), osum, 0, 0, 0);
+        osum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(one4), osum, 0, 0, 0);
+        return;
+      }
+      // V^T column blocks of 16 dims
 #pragma unroll
       for (int nb = 0; nb < kNBlocks; ++nb) {
         uint4 vw;
@@ -612,6 +784,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         x[h] = reduce_lane_bits<log2_int(kT), false>(x[h]);  // add the parts of D
+        if constexpr (kInt4) x[h] = (x[h] - q8[h]) * row_ks;  // q.(u - 8), the row's K scale
         x[h] = ok ? x[h] * c2 : -INFINITY;
         const float mt = row_reduce16<true>(x[h]);
         float tile_max = lane_value(mt, 0);
@@ -625,8 +798,10 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
         x[h] = p;
       }
       if (part == 0) {
+        // INT4: p times the row's V scale and 2^9 (the V codes convert to
+        // n * 2^-9; rows past the sequence have scale 0 and p 0)
 #pragma unroll
-        for (int h = 0; h < G; ++h) pt[n * G + h] = x[h];
+        for (int h = 0; h < G; ++h) pt[n * G + h] = kInt4 ? x[h] * (row_vs * 512.0f) : x[h];
       }
       wave_lds_fence();
 
@@ -644,7 +819,9 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 #pragma unroll
         for (int h = 0; h < G; ++h) ph[h] = pt[r * G + h];
         float vf[8];
-        if constexpr (kFp8) {
+        if constexpr (kInt4) {
+          int4x8_to_f32_scaled(vr[m], vf);
+        } else if constexpr (kFp8) {
           e4m3x8_to_f32(vr[m], vf);
         } else {
           const uint32_t vw[4] = {vr[m].x, vr[m].y, vr[m].z, vr[m].w};
@@ -686,11 +863,22 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   if constexpr (kMfmaPv) {
     l_sum = reduce_lane_bits<4, false>(l_sum);  // lane n: head n's sum over the wave's rows
     if (lane < 4 * G) {                          // lane groups holding real heads
+      if constexpr (kInt4) {
+        // p.(u - 8) = p.u - 8 sum(p)
+        const int d0 = 16 * ((lane & 15) >> 3) + 2 * (lane & 7);
 #pragma unroll
-      for (int nb = 0; nb < kNBlocks; ++nb)
+        for (int nb = 0; nb < kNBlocks; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          wst[(4 * (lane >> 4) + r) * D + 16 * nb + (lane & 15)] = oacc[nb][r];
+          for (int r = 0; r < 4; ++r)
+            wst[(4 * (lane >> 4) + r) * D + 32 * (nb >> 1) + d0 + (nb & 1)] =
+                oacc[nb][r] - 8.f * osum[r];
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < kNBlocks; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            wst[(4 * (lane >> 4) + r) * D + 16 * nb + (lane & 15)] = oacc[nb][r];
+      }
     }
     if (lane < G) {
       wst_ml[wave * 2 * G + lane] = m_lane;
@@ -1069,13 +1257,13 @@ __global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int D, int G, bool kFp8, bool kPaged>
+template <int D, int G, int kKv, bool kPaged>
 static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipStream_t st) {
   // Dynamic LDS that brings the workgroup's total to kOnePerCuLds, more than
   // half a CU's LDS, so no second workgroup fits on the CU and the streaming
   // workgroups spread over all CUs instead of doubling up on some.  The
   // static part already counts toward the total.
-  constexpr int kStatic = split_smem_bytes<D, G, kFp8>() + kWaves * 2 * G * 4 + 64;
+  constexpr int kStatic = split_smem_bytes<D, G, kKv>() + kWaves * 2 * G * 4 + 64;
   static_assert(kStatic + 0 <= kMaxLdsPerWorkgroup, "static LDS over the limit");
   constexpr int kPad = kStatic < kOnePerCuLds ? kOnePerCuLds - kStatic : 0;
   static_assert(kStatic + kPad <= kMaxLdsPerWorkgroup, "padded LDS over the limit");
@@ -1084,45 +1272,52 @@ static hipError_t launch_split(int B, const SplitArgs& a, bool one_per_cu, hipSt
   static const int static_lds = [] {
     hipFuncAttributes fa;
     if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
-                                      &split_kv_decode_kernel<D, G, kFp8, kPaged>)) != hipSuccess)
+                                      &split_kv_decode_kernel<D, G, kKv, kPaged>)) != hipSuccess)
       return -1;
     return (int)fa.sharedSizeBytes;
   }();
   const bool pad_fits = static_lds >= 0 && static_lds + kPad <= kMaxLdsPerWorkgroup;
   dim3 grid((unsigned)(a.ns | 1), (unsigned)a.Hkv, (unsigned)B);
-  hipLaunchKernelGGL((split_kv_decode_kernel<D, G, kFp8, kPaged>), grid, dim3(kThreads),
+  hipLaunchKernelGGL((split_kv_decode_kernel<D, G, kKv, kPaged>), grid, dim3(kThreads),
                      (unsigned)(one_per_cu && pad_fits ? kPad : 0), st, a);
   return hipGetLastError();
 }
 
-template <bool kFp8, bool kPaged>
+template <int kKv, bool kPaged>
 static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bool one_per_cu,
                                      hipStream_t st) {
   if (D == 128) {
     switch (G) {
-      case 1: return launch_split<128, 1, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 2: return launch_split<128, 2, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 4: return launch_split<128, 4, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 8: return launch_split<128, 8, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 1: return launch_split<128, 1, kKv, kPaged>(B, a, one_per_cu, st);
+      case 2: return launch_split<128, 2, kKv, kPaged>(B, a, one_per_cu, st);
+      case 4: return launch_split<128, 4, kKv, kPaged>(B, a, one_per_cu, st);
+      case 8: return launch_split<128, 8, kKv, kPaged>(B, a, one_per_cu, st);
     }
   } else if (D == 64) {
     switch (G) {
-      case 1: return launch_split<64, 1, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 2: return launch_split<64, 2, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 4: return launch_split<64, 4, kFp8, kPaged>(B, a, one_per_cu, st);
-      case 8: return launch_split<64, 8, kFp8, kPaged>(B, a, one_per_cu, st);
+      case 1: return launch_split<64, 1, kKv, kPaged>(B, a, one_per_cu, st);
+      case 2: return launch_split<64, 2, kKv, kPaged>(B, a, one_per_cu, st);
+      case 4: return launch_split<64, 4, kKv, kPaged>(B, a, one_per_cu, st);
+      case 8: return launch_split<64, 8, kKv, kPaged>(B, a, one_per_cu, st);
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_split_kv_decode(int D, int G, bool fp8, bool paged, int B, const SplitArgs& a,
-                                  bool one_per_cu, hipStream_t st) {
-  if (paged)
-    return fp8 ? launch_split_typed<true, true>(D, G, B, a, one_per_cu, st)
-               : launch_split_typed<false, true>(D, G, B, a, one_per_cu, st);
-  return fp8 ? launch_split_typed<true, false>(D, G, B, a, one_per_cu, st)
-             : launch_split_typed<false, false>(D, G, B, a, one_per_cu, st);
+hipError_t launch_split_kv_decode(int D, int G, int kv_format, bool paged, int B,
+                                  const SplitArgs& a, bool one_per_cu, hipStream_t st) {
+  switch (kv_format) {
+    case kKvBf16:
+      return paged ? launch_split_typed<kKvBf16, true>(D, G, B, a, one_per_cu, st)
+                   : launch_split_typed<kKvBf16, false>(D, G, B, a, one_per_cu, st);
+    case kKvE4m3:
+      return paged ? launch_split_typed<kKvE4m3, true>(D, G, B, a, one_per_cu, st)
+                   : launch_split_typed<kKvE4m3, false>(D, G, B, a, one_per_cu, st);
+    case kKvInt4:
+      if (paged) return hipErrorInvalidValue;
+      return launch_split_typed<kKvInt4, false>(D, G, B, a, one_per_cu, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st) {

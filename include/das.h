@@ -73,9 +73,10 @@ typedef enum {
   DAS_ELAUNCH = -4,    /* the HIP runtime refused a launch or a device query */
 } das_status;
 
-/* Element types.  Outputs are DAS_F32 or DAS_BF16; a K/V cache is DAS_BF16
- * or DAS_E4M3 (OCP 8-bit floating point, see das_decode_attention_fp8). */
-typedef enum { DAS_F32 = 0, DAS_BF16 = 1, DAS_E4M3 = 2 } das_dtype;
+/* Element types.  Outputs are DAS_F32 or DAS_BF16; a K/V cache is DAS_BF16,
+ * DAS_E4M3 (OCP 8-bit floating point, see das_decode_attention_fp8) or
+ * DAS_INT4 (4-bit integers with row scales, see das_decode_attention_int4). */
+typedef enum { DAS_F32 = 0, DAS_BF16 = 1, DAS_E4M3 = 2, DAS_INT4 = 3 } das_dtype;
 
 /* Page-pool layouts of a paged K/V cache (see das_decode_attention_paged). */
 typedef enum {
@@ -202,13 +203,51 @@ int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_ca
                             void* stream);
 
 /*
+ * Decode attention over a 4-bit integer K/V cache ([FD++] §4 names INT4
+ * beside FP8: a quarter of the bf16 bytes, dequantised on chip).  The pages
+ * leave the code and its scaling open; this library reads them as
+ * two's-complement 4-bit integers (-8 ... 7), two per byte, element 2i in
+ * the low nibble and element 2i+1 in the high nibble, with one fp32 scale per
+ * cached row (batch row, kv-head, token) for K and one for V:
+ *   K[b][g][j][d] = k_scale[b][g][j] * int4(element d of k_cache[b][g][j]),
+ *   V likewise.
+ *   k_cache, v_cache  uint8 [B][Hkv][Smax][D/2]
+ *   k_scale, v_scale  device float [B][Hkv][Smax], 4-byte aligned (only the
+ *                     rows j < seq_lens[b] are read)
+ * Everything else (q, seq_lens, out, lse_out, num_splits, workspace and its
+ * precondition, stream, supported shapes, errors) is as for
+ * das_decode_attention; the plan and das_decode_workspace_bytes are shared.
+ * The codes become exact bf16 integers on chip; a row's K scale multiplies its
+ * finished dot product and its V scale its softmax weight.  A sequence's rows
+ * are addressed with 32-bit byte offsets: (Smax + 256) * D / 2 < 2^31.  NULL
+ * or misaligned k_scale or v_scale: DAS_EINVAL.  There is no paged INT4 cache
+ * (das_decode_attention_paged returns DAS_ENOTSUP for DAS_INT4).
+ */
+int das_decode_attention_int4(const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                              float scale, void* out, int32_t out_dtype, float* lse_out,
+                              int32_t num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Phase 1 alone over an INT4 K/V cache: das_split_kv_decode with the cache
+ * of das_decode_attention_int4.  Finish with das_lse_combine. */
+int das_split_kv_decode_int4(const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                             float scale, void* out, int32_t out_dtype, float* lse_out,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Decode attention over a paged K/V cache ([FD++] §6).  K and V live in two
  * page pools of num_pages pages of page_size rows; row j of sequence b is
  * row j % page_size of page block_table[b][j / page_size]:
  *   k_pool, v_pool  [num_pages][Hkv][page_size][D] (DAS_PAGED_HND) or
  *                   [num_pages][page_size][Hkv][D] (DAS_PAGED_NHD), elements
  *                   of kv_dtype: DAS_BF16, or DAS_E4M3 with k_scale/v_scale
- *                   as in das_decode_attention_fp8 (ignored for DAS_BF16)
+ *                   as in das_decode_attention_fp8 (ignored for DAS_BF16);
+ *                   DAS_INT4: DAS_ENOTSUP
  *   block_table     device int32 [B][max_blocks]; entries of pages a sequence
  *                   does not reach are never read; an entry outside
  *                   [0, num_pages) is clamped into it on the device (wrong

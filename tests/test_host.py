@@ -166,6 +166,42 @@ def test_fp8_row_bound_is_twice_the_bf16_one(lib):
     assert _call_decode_fp8(lib, Smax=smax, ws=0) == das.DAS_EWORKSPACE
 
 
+def _call_decode_int4(lib, **kw):
+    a = dict(q=16, k=16, v=16, ks=16, vs=16, sl=16, B=1, Hq=8, Hkv=2, Smax=1024, D=128, scale=0.1,
+             out=16, dt=0, lse=0, ns=4, ws=16, wsb=1 << 30, st=None)
+    a.update(kw)
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.das_decode_attention_int4(P(a["q"]), P(a["k"]), P(a["v"]), P(a["ks"]), P(a["vs"]),
+                                         P(a["sl"]), a["B"], a["Hq"], a["Hkv"], a["Smax"], a["D"],
+                                         a["scale"], P(a["out"]), a["dt"], P(a["lse"]), a["ns"],
+                                         P(a["ws"]), a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0), das.DAS_EINVAL), (dict(vs=0), das.DAS_EINVAL),
+    (dict(ks=18), das.DAS_EINVAL), (dict(vs=17), das.DAS_EINVAL),      # scales 4-byte aligned
+    (dict(q=0), das.DAS_EINVAL), (dict(k=0), das.DAS_EINVAL), (dict(v=8), das.DAS_EINVAL),
+    (dict(Hq=6, Hkv=2), das.DAS_ENOTSUP), (dict(D=80), das.DAS_ENOTSUP),
+    (dict(ws=0), das.DAS_EWORKSPACE),
+    (dict(Smax=(1 << 25)), das.DAS_ENOTSUP),        # 32-bit row offsets: (Smax+256)*D/2 >= 2^31
+])
+def test_decode_int4_argument_checks(lib, kw, status):
+    # All pointers are fake: a failed check must return before any launch.
+    assert _call_decode_int4(lib, **kw) == status
+
+
+def test_int4_row_bound_is_four_times_the_bf16_one(lib):
+    # D/2-byte rows allow four times the bf16 rows before the 32-bit offsets
+    # run out; the int4 call then fails only on the missing workspace.
+    smax = 1 << 24
+    assert _call_decode_fp8(lib, Smax=smax, ws=0) == das.DAS_ENOTSUP
+    assert _call_decode_int4(lib, Smax=smax, ws=0) == das.DAS_EWORKSPACE
+
+
+def test_paged_int4_is_not_supported(lib):
+    assert _call_paged(lib, kvt=das.DAS_INT4, ks=16, vs=16) == das.DAS_ENOTSUP
+
+
 def test_merge_argument_checks(lib):
     P = ctypes.c_void_p
     f = lib.das_merge_attn_states
