@@ -385,6 +385,37 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   if (s >= a.ns) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+
+  // ---- the query rows, loaded first: their latency overlaps that of the
+  // sequence length and the issue of the first K/V tile ----
+  // G >= 4: lane i loads, for k-block kb, the 8 dims of chunk 4*kb + i/16 of
+  //         head i%16 (zero when >= G; INT4: chunk (i/16)*kKBlocks + kb, the
+  //         lane's K bytes being contiguous).
+  // G <= 2: lane i loads the part i / kT of D of every head.
+  constexpr int kParts = 64 / kT;
+  constexpr int kPartDims = D / kParts;
+  constexpr int kQRegs = G >= 4 ? kKBlocks : G * (kPartDims / 8);
+  uint4 qraw[kQRegs];
+  if constexpr (G >= 4) {
+    const int hh = lane & 15;
+    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + (hh < G ? hh : 0)) * D;
+#pragma unroll
+    for (int kb = 0; kb < kKBlocks; ++kb) {
+      const int c = kInt4 ? (lane >> 4) * kKBlocks + kb : 4 * kb + (lane >> 4);
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+      qraw[kb] = hh < G ? w : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    const int part = lane / kT;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          a.q + ((size_t)b * a.Hq + (size_t)g * G + h) * D + part * kPartDims);
+#pragma unroll
+      for (int i = 0; i < kPartDims / 8; ++i) qraw[h * (kPartDims / 8) + i] = qrow[i];
+    }
+  }
+
   const int L = clamp_len(a.seq_lens[b], a.Smax);
   // The sequence's rows are cut into chunks of a.chunk rows; split s owns
   // chunk s (chunk * ns >= Smax, so every row has a split).
@@ -430,64 +461,16 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     v_scale = a.v_scale[g];
   }
 
-  // ---- query operand ----
-  // G >= 4: MFMA B operand (q^T); lane i holds head i%16 (zero when >= G)
-  //         and, for k-block kb, the 8 dims of chunk 4*kb + i/16 (INT4:
-  //         chunk (i/16)*kKBlocks + kb, the lane's K bytes being contiguous).
-  // G <= 2: lane i works on row i % kT and the part i / kT of D; it
-  //         holds that part of every head as bf16 pairs.
+  // ---- query operand (filled from qraw once the first tile is issued) ----
+  // G >= 4: MFMA B operand (q^T); lane i holds head i%16 and the dims it
+  //         loaded.  G <= 2: lane i works on row i % kT and the part i / kT
+  //         of D; it holds that part of every head as bf16 pairs.
   // INT4 codes convert in the order 0, 2, 4, 6, 1, 3, 5, 7 within each
   // group of 8 dims, so q's dims are held in that order too, and the sum of
   // q over D is kept to take off the codes' offset: (q.(u - 8)) = q.u - 8 sum(q).
-  constexpr int kParts = 64 / kT;
-  constexpr int kPartDims = D / kParts;
   bf16x8_t qa[kKBlocks];
   uint32_t qv[G <= 2 ? G : 1][G <= 2 ? kPartDims / 2 : 1];
   float q8[G <= 2 ? G : 1];     // INT4: 8 * sum(q) per head (G >= 4: the lane's head)
-  auto bf16x8_sum = [](uint4 w) {
-    return ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
-           ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
-  };
-  if constexpr (G >= 4) {
-    const int hh = lane & 15;
-    float qs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kKBlocks; ++kb) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (hh < G) {
-        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + (size_t)g * G + hh) * D;
-        const int c = kInt4 ? (lane >> 4) * kKBlocks + kb : 4 * kb + (lane >> 4);
-        w = *reinterpret_cast<const uint4*>(qrow + 8 * c);
-      }
-      if constexpr (kInt4) {
-        qs += bf16x8_sum(w);
-        w = bf16x8_even_odd(w);
-      }
-      qa[kb] = as_bf16x8(w);
-    }
-    if constexpr (kInt4) q8[0] = 8.f * reduce_lane_bits<4, false>(qs);
-  } else {
-    const int part = lane / kT;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4* qrow = reinterpret_cast<const uint4*>(
-          a.q + ((size_t)b * a.Hq + (size_t)g * G + h) * D + part * kPartDims);
-      float qs = 0.f;
-#pragma unroll
-      for (int i = 0; i < kPartDims / 8; ++i) {
-        uint4 w = qrow[i];
-        if constexpr (kInt4) {
-          qs += bf16x8_sum(w);
-          w = bf16x8_even_odd(w);
-        }
-        qv[h][4 * i + 0] = w.x;
-        qv[h][4 * i + 1] = w.y;
-        qv[h][4 * i + 2] = w.z;
-        qv[h][4 * i + 3] = w.w;
-      }
-      if constexpr (kInt4) q8[h] = 8.f * reduce_lane_bits<log2_int(kT), false>(qs);
-    }
-  }
 
   // ---- per-wave running state (maxima in base-2 units) ----
   // G <= 2: wave-uniform running max per head, this lane's exponential sums,
@@ -595,6 +578,63 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     }
   };
 
+  // G >= 4: the tiles go through registers, one tile ahead of the one being
+  // processed.  fetch_tile loads tile r0 -- what the LDS-direct loads of
+  // load_tile would write at [m KiB + 16 lane] of the K and V tiles, and the
+  // INT4 row scales (lanes 0..kT-1 K, kT..63 V) -- and stage_tile writes it
+  // into the wave's LDS tiles once the previous tile has been processed.
+  // The next tile's loads are thus in flight while the current one is
+  // processed, instead of the wave issuing nothing during that time.
+  struct TileRegs {
+    uint4 k[kMfmaPv ? kKLoads : 1];
+    uint4 v[kMfmaPv ? kKLoads : 1];
+    float sc;
+  };
+  auto fetch_tile = [&](int r0, TileRegs& t, int page) {
+    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
+    int soff = r0 * kRowBytes;
+    if constexpr (kInt4) {
+      if (lane < kT)
+        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, r0 * 4, 0));
+      else
+        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane - kT) * 4, r0 * 4, 0));
+    }
+    if constexpr (kPaged) {
+      const int slot = r0 >> a.page_shift;
+      page = min(max(page, 0), a.num_pages - 1);
+      const int p0 = slot << a.page_shift;
+      const int nvalid = min(L - p0, 1 << a.page_shift);
+      const size_t off = (size_t)page * (size_t)a.page_bytes + (size_t)g * (size_t)a.head_stride;
+      const int bytes = (nvalid - 1) * row_stride + kRowBytes;
+      rk = make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + off, bytes);
+      rv = make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + off, bytes);
+      soff = (r0 - p0) * row_stride;
+    }
+#pragma unroll
+    for (int m = 0; m < kKLoads; ++m) {
+      const int r = kKRowsPerLoad * m + k_row_in_load;
+      const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
+      t.k[m] = buffer_load16(rk, r * row_stride + 16 * c, soff);
+    }
+#pragma unroll
+    for (int m = 0; m < kKLoads; ++m) {
+      const int r = kKRowsPerLoad * m + k_row_in_load;
+      const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
+      t.v[m] = buffer_load16(rv, r * row_stride + 16 * c, soff);
+    }
+  };
+  auto stage_tile = [&](const TileRegs& t, unsigned char* kbuf) {
+    wave_lds_fence();   // the previous tile's LDS reads come first
+#pragma unroll
+    for (int m = 0; m < kKLoads; ++m)
+      *reinterpret_cast<uint4*>(kbuf + m * 1024 + 16 * lane) = t.k[m];
+#pragma unroll
+    for (int m = 0; m < kKLoads; ++m)
+      *reinterpret_cast<uint4*>(kbuf + kKTileBytes + m * 1024 + 16 * lane) = t.v[m];
+    if constexpr (kInt4) reinterpret_cast<float*>(kbuf + 2 * kKTileBytes)[lane] = t.sc;
+    wave_lds_fence();
+  };
+
   // Elements 8*grp8 .. 8*grp8+7 of row r of a K tile, as bf16 (INT4: the
   // offset codes u, in the order 0, 2, 4, 6, 1, 3, 5, 7).
   auto k_group = [&](const unsigned char* ktile, int r, int grp8) -> uint4 {
@@ -613,9 +653,7 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   auto process_tile = [&](int r0, const VReg* vr, const unsigned char* ktile) {
     if constexpr (kMfmaPv) {
-      // K and V both arrive through LDS
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      wave_lds_fence();
+      // K and V are in LDS (staged by stage_tile)
       const unsigned char* vtile = ktile + kKTileBytes;
       const int n = lane & 15, grp = lane >> 4;
       // INT4: the tile's row scales (K at [0, kT), V at [kT, 2 kT))
@@ -845,13 +883,80 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   const int row_lo = s * a.chunk;
   row_end = min(row_lo + a.chunk, L);
   int r0 = row_lo + wave * kT;
-  int page_next = (kPaged && r0 < row_end) ? page_of(r0) : 0;
-  for (; r0 < row_end; r0 += stride) {
-    const int page = page_next;
+  VReg vr[kLoads];
+  TileRegs tr;
+  int page_next = 0;
+  if (r0 < row_end) {
+    const int page = kPaged ? page_of(r0) : 0;
     if (kPaged && r0 + stride < row_end) page_next = page_of(r0 + stride);
-    VReg vr[kLoads];
-    load_tile(r0, vr, kt, page);
-    process_tile(r0, vr, kt);
+    if constexpr (kMfmaPv)
+      fetch_tile(r0, tr, page);
+    else
+      load_tile(r0, vr, kt, page);
+  }
+
+  // The query operand, from the rows loaded at the start (issued before the
+  // tile, so waiting for them leaves the tile in flight).
+  auto bf16x8_sum = [](uint4 w) {
+    return ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
+           ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
+  };
+  if constexpr (G >= 4) {
+    float qs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kKBlocks; ++kb) {
+      uint4 w = qraw[kb];
+      if constexpr (kInt4) {
+        qs += bf16x8_sum(w);
+        w = bf16x8_even_odd(w);
+      }
+      qa[kb] = as_bf16x8(w);
+    }
+    if constexpr (kInt4) q8[0] = 8.f * reduce_lane_bits<4, false>(qs);
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float qs = 0.f;
+#pragma unroll
+      for (int i = 0; i < kPartDims / 8; ++i) {
+        uint4 w = qraw[h * (kPartDims / 8) + i];
+        if constexpr (kInt4) {
+          qs += bf16x8_sum(w);
+          w = bf16x8_even_odd(w);
+        }
+        qv[h][4 * i + 0] = w.x;
+        qv[h][4 * i + 1] = w.y;
+        qv[h][4 * i + 2] = w.z;
+        qv[h][4 * i + 3] = w.w;
+      }
+      if constexpr (kInt4) q8[h] = 8.f * reduce_lane_bits<log2_int(kT), false>(qs);
+    }
+  }
+
+  // Stream.  G >= 4: stage the fetched tile, fetch the wave's next one,
+  // process the staged one.  G <= 2: process the tile in flight, then issue
+  // the next one.
+  if constexpr (kMfmaPv) {
+    for (; r0 < row_end; r0 += stride) {
+      stage_tile(tr, kt);
+      const int rn = r0 + stride;
+      if (rn < row_end) {
+        const int page = page_next;
+        if (kPaged && rn + stride < row_end) page_next = page_of(rn + stride);
+        fetch_tile(rn, tr, page);
+      }
+      process_tile(r0, vr, kt);
+    }
+  } else {
+    for (; r0 < row_end; r0 += stride) {
+      process_tile(r0, vr, kt);
+      const int rn = r0 + stride;
+      if (rn < row_end) {
+        const int page = page_next;
+        if (kPaged && rn + stride < row_end) page_next = page_of(rn + stride);
+        load_tile(rn, vr, kt, page);
+      }
+    }
   }
 
   // ---- end of the stream: each wave's state into its own tile region ----
