@@ -21,13 +21,16 @@
 //     slots of the A operand of p.V, with no data movement.  p is split into
 //     two bf16 halves (p = hi + lo to about 2^-18 relative), so p.V keeps
 //     fp32-level accuracy; V is exact in bf16 (and so is E4M3).  K and V go
-//     from HBM straight into a per-wave LDS tile with an XOR swizzle; K is
-//     read one row per lane, V column-wise with the gfx950 transposing LDS
-//     reads (ds_read_b64_tr_b16 / _tr_b8), both free of bank conflicts.
+//     through a per-wave LDS tile with an XOR swizzle, staged from registers
+//     one tile ahead (a wave's next tile is in flight while it processes the
+//     current one); K is read one row per lane, V column-wise with the
+//     gfx950 transposing LDS reads (ds_read_b64_tr_b16 / _tr_b8), both free
+//     of bank conflicts.
 //   * For G in {1, 2} q.K^T is a matrix-vector product on the vector ALUs
 //     (v_dot2_f32_bf16: exact bf16 products, fp32 accumulation), and p.V runs
 //     on the vector ALUs in fp32 straight from the coalesced V registers; p
-//     reaches the lanes that need it through a small per-wave LDS buffer.
+//     reaches the lanes that need it through a small per-wave LDS buffer.  K
+//     goes from HBM straight into the LDS tile (buffer_load ... lds).
 //   * The online softmax keeps, per wave and head, a running max (base-2
 //     units: logits are scaled by scale*log2(e) in fp32 after the dot) and
 //     rescales the partial sums only when the max grows.
@@ -498,12 +501,13 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
   for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t osum = {0.f, 0.f, 0.f, 0.f};
 
-  // K goes from HBM straight into the wave's LDS tile (buffer_load ... lds):
-  // load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the tile, lane l the
-  // 16 bytes at 16*l, i.e. row kKRowsPerLoad*m + k_row_in_load, slot k_slot.
-  // The lane fetches the logical chunk whose swizzled slot that is, so the
-  // tile ends up in the k_tile_offset layout.  G >= 4: V goes the same way
-  // into the V tile that follows; G <= 2: V goes to registers.
+  // A K tile in LDS: load m fills the 1 KiB slab [m KiB, (m+1) KiB) of the
+  // tile, lane l the 16 bytes at 16*l, i.e. row kKRowsPerLoad*m +
+  // k_row_in_load, slot k_slot.  The lane fetches the logical chunk whose
+  // swizzled slot that is, so the tile ends up in the k_tile_offset layout.
+  // G >= 4: V is laid out the same way in the V tile that follows (both
+  // staged from registers by stage_tile); G <= 2: K is loaded straight into
+  // LDS (buffer_load ... lds) and V goes to registers.
   using VReg = typename std::conditional<
       kInt4, uint32_t, typename std::conditional<kFp8, uint2, uint4>::type>::type;
   // INT4, G <= 2: the K and V scales of this lane's row (lane % kT) of the tile
@@ -518,22 +522,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
     return table[(size_t)b * a.max_blocks + (r >> a.page_shift)];
   };
 
+  // G <= 2: K straight into the wave's LDS tile, V (and INT4 row scales)
+  // into registers.
   auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf, int page) {
     __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
     int soff = r0 * kRowBytes;
     if constexpr (kInt4) {
-      // row scales first, so that waiting for K also covers them
-      if constexpr (kMfmaPv) {
-        // one dword per row into the scale area: lanes 0..31 K, 32..63 V
-        auto* sdst = (__attribute__((address_space(3))) void*)(kbuf + 2 * kKTileBytes);
-        if (lane < kT)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, sdst, 4, lane * 4, r0 * 4, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, sdst, 4, (lane - kT) * 4, r0 * 4, 0, 0);
-      } else {
-        row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (lane % kT) * 4, r0 * 4, 0));
-        row_vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane % kT) * 4, r0 * 4, 0));
-      }
+      row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (lane % kT) * 4, r0 * 4, 0));
+      row_vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane % kT) * 4, r0 * 4, 0));
     }
     if constexpr (kPaged) {
       // this tile's page; a table entry outside the pool is clamped into it
@@ -556,25 +552,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
           rk, (__attribute__((address_space(3))) void*)(kbuf + m * 1024), 16,
           r * row_stride + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
     }
-    if constexpr (kMfmaPv) {
 #pragma unroll
-      for (int m = 0; m < kKLoads; ++m) {
-        const int r = kKRowsPerLoad * m + k_row_in_load;
-        const int c = k_slot ^ ((r / (256 / kRowBytes)) % kKLanesPerRow);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(kbuf + kKTileBytes + m * 1024), 16,
-            r * row_stride + 16 * c, soff, 0, DAS_KV_CACHE_POLICY);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < kLoads; ++m) {
-        if constexpr (kInt4)
-          vr[m] = buffer_load4(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
-        else if constexpr (kFp8)
-          vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
-        else
-          vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
-      }
+    for (int m = 0; m < kLoads; ++m) {
+      if constexpr (kInt4)
+        vr[m] = buffer_load4(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+      else if constexpr (kFp8)
+        vr[m] = buffer_load8(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
+      else
+        vr[m] = buffer_load16(rv, lane_off + m * kRowsPerLoad * row_stride, soff);
     }
   };
 
