@@ -181,7 +181,8 @@ def main():
     if paged is not None:
         # the paged plan: Smax = max_blocks * page size, chunks rounded up to whole pages
         Smax = paged.block_table.shape[1] * paged.page_size
-    ns, chunk = das.das_plan(B, Hkv, Hq // Hkv, Smax, D, args.splits)
+    kv_code = das.DAS_INT4 if int4 else (das.DAS_E4M3 if fp8 else das.DAS_BF16)
+    ns, chunk = das.das_plan_kv(kv_code, B, Hkv, Hq // Hkv, Smax, D, args.splits)
     if paged is not None and chunk % paged.page_size:
         chunk = -(-chunk // paged.page_size) * paged.page_size
         ns = -(-Smax // chunk)

@@ -25,7 +25,7 @@ DAS_MAX_SPLITS = 4096
 DAS_CHUNK_QUANTUM = 128
 DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 
-EXPORTED = ("das_plan", "das_decode_workspace_bytes", "das_decode_attention",
+EXPORTED = ("das_plan", "das_plan_kv", "das_decode_workspace_bytes", "das_decode_attention",
             "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
             "das_decode_attention_int4", "das_split_kv_decode_int4", "das_decode_attention_paged", "das_lse_combine", "das_merge_attn_states",
             "das_strerror")
@@ -52,6 +52,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     pi32 = ctypes.POINTER(ctypes.c_int32)
     lib.das_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, pi32, pi32]
     lib.das_plan.restype = ctypes.c_int
+    lib.das_plan_kv.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, pi32, pi32]
+    lib.das_plan_kv.restype = ctypes.c_int
     lib.das_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.das_decode_workspace_bytes.restype = sz
     decode_args = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_float, p, i32, p, i32, p, sz, p]
@@ -92,6 +94,16 @@ def das_plan(B: int, Hkv: int, G: int, Smax: int, D: int, num_splits: int = 0,
     ns, chunk = ctypes.c_int32(), ctypes.c_int32()
     _check(load_library().das_plan(B, Hkv, G, Smax, D, num_splits, num_cus,
                                    ctypes.byref(ns), ctypes.byref(chunk)), "das_plan")
+    return ns.value, chunk.value
+
+
+def das_plan_kv(kv_dtype: int, B: int, Hkv: int, G: int, Smax: int, D: int, num_splits: int = 0,
+                num_cus: int = 0) -> Tuple[int, int]:
+    """(number of splits, rows per split) of the one-call entry point for a
+    K/V cache of kv_dtype (DAS_BF16, DAS_E4M3 or DAS_INT4)."""
+    ns, chunk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().das_plan_kv(kv_dtype, B, Hkv, G, Smax, D, num_splits, num_cus,
+                                      ctypes.byref(ns), ctypes.byref(chunk)), "das_plan_kv")
     return ns.value, chunk.value
 
 

@@ -27,6 +27,11 @@ std::atomic<int> g_cu_cache[kMaxDevices];
 // fewer, longer splits cut the partial results and the per-workgroup start
 // and end latencies (32K-row GQA decode: 24 splits 28.5 us, 32 splits 30.7 us).
 constexpr int64_t kTargetWgsPer4Cus = 3;
+// An INT4 cache moves a quarter of the bytes per row, so its call is bound
+// by the per-row work on the CUs rather than by HBM, and the fused call aims
+// for one workgroup on every CU (128K-row GQA decode: 24 splits 44.3 us, 32
+// splits 35.0 us; an E4M3 cache measured the same with either plan).
+constexpr int64_t kTargetWgsPer4CusInt4 = 4;
 constexpr int64_t kMaxChunk = 8192;
 // Even when the batch alone fills the chip, a maximal-length sequence is cut
 // into at least this many splits, so that with variable lengths the last
@@ -71,8 +76,13 @@ int device_cus(int32_t num_cus, int* out) {
   return DAS_OK;
 }
 
+int64_t wgs_for_format(int format) {
+  return format == das::kKvInt4 ? kTargetWgsPer4CusInt4 : kTargetWgsPer4Cus;
+}
+
 int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t num_splits,
-              int32_t num_cus, int32_t* ns_out, int32_t* chunk_out) {
+              int32_t num_cus, int32_t* ns_out, int32_t* chunk_out,
+              int64_t wgs_per_4cus = kTargetWgsPer4Cus) {
   if (B < 1 || B > 65535 || Hkv < 1 || Hkv > 65535 || G < 1 || Smax < 1 || D < 1 ||
       num_splits < 0 || num_cus < 0)
     return DAS_EINVAL;
@@ -86,7 +96,7 @@ int plan_impl(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_
     const int rc = device_cus(num_cus, &cus);
     if (rc != DAS_OK) return rc;
     const int64_t units = (int64_t)B * Hkv;
-    const int64_t target = std::max<int64_t>(1, kTargetWgsPer4Cus * cus / 4);
+    const int64_t target = std::max<int64_t>(1, wgs_per_4cus * cus / 4);
     int64_t ns_fill = ceil_div(target, units);
     if (ns_fill < kMinSplitsLongest) ns_fill = kMinSplitsLongest;
     chunk = round_up(ceil_div(Smax, ns_fill), DAS_CHUNK_QUANTUM);
@@ -146,7 +156,7 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
                  int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D, float scale, const void* out,
                  int32_t out_dtype, int32_t num_splits, const void* workspace,
                  size_t workspace_bytes, bool need_inputs, int64_t row_bytes, Checked* c,
-                 int32_t page_size = 0) {
+                 int32_t page_size = 0, int64_t wgs_per_4cus = kTargetWgsPer4Cus) {
   if (seq_lens == nullptr || out == nullptr) return DAS_EINVAL;
   if (need_inputs && (q == nullptr || k == nullptr || v == nullptr)) return DAS_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || D < 1) return DAS_EINVAL;
@@ -161,7 +171,7 @@ int check_decode(const void* q, const void* k, const void* v, const int32_t* seq
   if (need_inputs && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return DAS_EINVAL;
   if (!aligned16(out) || ((uintptr_t)seq_lens & 3u) != 0) return DAS_EINVAL;
   int32_t ns = 0, chunk = 0;
-  const int rc = plan_impl(B, Hkv, G, Smax, D, num_splits, 0, &ns, &chunk);
+  const int rc = plan_impl(B, Hkv, G, Smax, D, num_splits, 0, &ns, &chunk, wgs_per_4cus);
   if (rc != DAS_OK) return rc;
   if (page_size > 0 && chunk % page_size != 0) {
     // a paged cache's chunks are whole pages: fewer, longer splits, so the
@@ -271,9 +281,11 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
                 float* lse_out, int32_t num_splits, void* workspace, size_t workspace_bytes,
                 void* stream) {
   Checked c{};
+  // the fused call's plan for this cache format (das_plan_kv); the
+  // phase-1-only entry points keep das_plan's, which das_lse_combine assumes
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
                               num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c,
-                              kv.page_size);
+                              kv.page_size, wgs_for_format(kv.format));
   if (rc != DAS_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One launch: the last workgroup of each (b, kv-head) merges the splits.
@@ -303,13 +315,33 @@ int das_plan(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t
   return plan_impl(B, Hkv, G, Smax, D, num_splits, num_cus, ns_out, chunk_out);
 }
 
+int das_plan_kv(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D,
+                int32_t num_splits, int32_t num_cus, int32_t* ns_out, int32_t* chunk_out) {
+  if (ns_out == nullptr || chunk_out == nullptr) return DAS_EINVAL;
+  int format;
+  switch (kv_dtype) {
+    case DAS_BF16: format = das::kKvBf16; break;
+    case DAS_E4M3: format = das::kKvE4m3; break;
+    case DAS_INT4: format = das::kKvInt4; break;
+    default: return DAS_EINVAL;
+  }
+  return plan_impl(B, Hkv, G, Smax, D, num_splits, num_cus, ns_out, chunk_out,
+                   wgs_for_format(format));
+}
+
 size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
                                   int32_t num_splits, int32_t num_cus) {
   if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return (size_t)-1;
-  int32_t ns = 0, chunk = 0;
-  if (plan_impl(B, Hkv, Hq / Hkv, Smax, D, num_splits, num_cus, &ns, &chunk) != DAS_OK)
-    return (size_t)-1;
-  return ws_total(B, Hq, ns, D);
+  // enough for the plan of every cache format (they differ only in the
+  // automatic plan's target)
+  size_t need = 0;
+  for (const int64_t target : {kTargetWgsPer4Cus, kTargetWgsPer4CusInt4}) {
+    int32_t ns = 0, chunk = 0;
+    if (plan_impl(B, Hkv, Hq / Hkv, Smax, D, num_splits, num_cus, &ns, &chunk, target) != DAS_OK)
+      return (size_t)-1;
+    need = std::max(need, ws_total(B, Hq, ns, D));
+  }
+  return need;
 }
 
 int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,

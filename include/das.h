@@ -110,11 +110,27 @@ int das_plan(int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D, int32_t
              int32_t num_cus, int32_t* ns_out, int32_t* chunk_out);
 
 /*
+ * The automatic plan of the one-call entry point for a K/V cache of
+ * kv_dtype (DAS_BF16, DAS_E4M3 or DAS_INT4; anything else: DAS_EINVAL).
+ * bf16 and E4M3 caches use das_plan's.  An INT4 cache aims for one workgroup
+ * on every compute unit instead of three per four: with a quarter of the
+ * bytes per row its call is bound by the work per row, not by HBM ([FD++] §2:
+ * fill the chip along the sequence axis).  A forced num_splits gives the same
+ * plan for every format.  The phase-1-only entry points
+ * (das_split_kv_decode*) always use das_plan's plan, which das_lse_combine
+ * assumes.  Arguments and outputs as for das_plan.
+ */
+int das_plan_kv(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t G, int32_t Smax, int32_t D,
+                int32_t num_splits, int32_t num_cus, int32_t* ns_out, int32_t* chunk_out);
+
+/*
  * Workspace bytes das_decode_attention needs for this shape and split
  * request (0 when the plan has a single split).  Layout: first
  * DAS_WORKSPACE_COUNTER_BYTES of arrival counters (one per (b, kv-head)),
  * then the phase-1 partial results of [FD++] §3: per (b, query head, split)
  * an unnormalised output row of D floats, then its max and exponential sum.
+ * The size covers the plan of every entry point and cache format for this
+ * shape (das_plan and das_plan_kv), so one workspace serves them all.
  * num_cus as in das_plan.  Returns (size_t)-1 on invalid arguments.
  */
 size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
@@ -216,7 +232,8 @@ int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_ca
  *                     rows j < seq_lens[b] are read)
  * Everything else (q, seq_lens, out, lse_out, num_splits, workspace and its
  * precondition, stream, supported shapes, errors) is as for
- * das_decode_attention; the plan and das_decode_workspace_bytes are shared.
+ * das_decode_attention, except that the automatic plan is das_plan_kv's for
+ * DAS_INT4 (one workgroup per compute unit); das_decode_workspace_bytes covers it.
  * The codes become exact bf16 integers on chip; a row's K scale multiplies its
  * finished dot product and its V scale its softmax weight.  A sequence's rows
  * are addressed with 32-bit byte offsets: (Smax + 256) * D / 2 < 2^31.  NULL

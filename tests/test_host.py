@@ -106,6 +106,29 @@ def test_workspace_bytes(lib):
         das.das_decode_workspace_bytes(1, 6, 4, 1024, 64, 0, 256)           # Hq % Hkv
 
 
+def test_plan_kv_int4_fills_every_cu_and_the_workspace_covers_it():
+    # bf16 and E4M3 share das_plan's plan; INT4 aims for one workgroup per CU
+    for shape in ((1, 8, 4, 32768, 128), (1, 8, 4, 131072, 128), (64, 8, 4, 16384, 128),
+                  (8, 8, 8, 100003, 128), (1, 8, 1, 1024, 64)):
+        base = plan(*shape)
+        assert das.das_plan_kv(das.DAS_BF16, *shape, 0, 256) == base
+        assert das.das_plan_kv(das.DAS_E4M3, *shape, 0, 256) == base
+    assert das.das_plan_kv(das.DAS_INT4, 1, 8, 4, 32768, 128, 0, 256) == (32, 1024)
+    assert das.das_plan_kv(das.DAS_INT4, 1, 8, 4, 131072, 128, 0, 256) == (32, 4096)
+    # a batch that already fills the chip keeps its plan
+    assert das.das_plan_kv(das.DAS_INT4, 64, 8, 4, 16384, 128, 0, 256) == plan(64, 8, 4, 16384, 128)
+    # forced splits: the same plan for every format
+    assert das.das_plan_kv(das.DAS_INT4, 1, 8, 4, 32768, 128, 7, 256) == \
+        das.das_plan(1, 8, 4, 32768, 128, 7, 256)
+    for Hq, Hkv, S, D in ((32, 8, 32768, 128), (32, 8, 131072, 128), (8, 8, 1024, 64)):
+        need = das.das_decode_workspace_bytes(1, Hq, Hkv, S, D, 0, 256)
+        for code in (das.DAS_BF16, das.DAS_INT4):
+            ns, _ = das.das_plan_kv(code, 1, Hkv, Hq // Hkv, S, D, 0, 256)
+            assert ns <= 1 or need >= das.DAS_WORKSPACE_COUNTER_BYTES + Hq * ns * (D + 2) * 4
+    with pytest.raises(das.DasError):
+        das.das_plan_kv(das.DAS_F32, 1, 8, 4, 1024, 128, 0, 256)
+
+
 def _call_decode(lib, **kw):
     a = dict(q=16, k=16, v=16, sl=16, B=1, Hq=8, Hkv=2, Smax=1024, D=128, scale=0.1, out=16,
              dt=0, lse=0, ns=4, ws=16, wsb=1 << 30, st=None)
