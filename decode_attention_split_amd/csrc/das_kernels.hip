@@ -638,51 +638,116 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
 
   auto process_tile = [&](int r0, const VReg* vr, const unsigned char* ktile) {
     if constexpr (kMfmaPv) {
-      // K and V are in LDS (staged by stage_tile)
+      // K and V are in LDS (staged by stage_tile).  Every LDS read of the
+      // tile is issued first, so their latency overlaps the q.K^T products
+      // and the softmax instead of stalling each product in turn.
       const unsigned char* vtile = ktile + kKTileBytes;
       const int n = lane & 15, grp = lane >> 4;
       // INT4: the tile's row scales (K at [0, kT), V at [kT, 2 kT))
       const float* sct = reinterpret_cast<const float*>(ktile + 2 * kKTileBytes);
-      // S^T = K q^T: lane l gets the logits of head n for rows 16*tg + 4*grp + r
-      float x[2][4];
+      // K: the 8 elements per k-block of rows 16*tg + n this lane feeds to
+      // the MFMA (INT4: the lane's kKBlocks * 4 contiguous bytes, one dword
+      // of 8 codes per k-block)
+      uint4 kraw[2][kKBlocks];
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kInt4) {
-          // the lane's kKBlocks * 4 contiguous bytes of row 16*tg + n: one
-          // dword (8 codes) per k-block
           constexpr int kLaneBytes = kKBlocks * 4;
           const unsigned char* kp = ktile +
                                     k_tile_offset<kRowBytes>(16 * tg + n, (grp * kLaneBytes) >> 4) +
                                     ((grp * kLaneBytes) & 15);
-          uint32_t kw[kKBlocks];
           if constexpr (kKBlocks == 4) {
             const uint4 t = *reinterpret_cast<const uint4*>(kp);
-            kw[0] = t.x; kw[1] = t.y; kw[2] = t.z; kw[3] = t.w;
+            kraw[tg][0].x = t.x; kraw[tg][1].x = t.y; kraw[tg][2].x = t.z; kraw[tg][3].x = t.w;
           } else {
             const uint2 t = *reinterpret_cast<const uint2*>(kp);
-            kw[0] = t.x; kw[1] = t.y;
+            kraw[tg][0].x = t.x; kraw[tg][1].x = t.y;
           }
-#pragma unroll
-          for (int kb = 0; kb < kKBlocks; ++kb)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(int4x8_to_bf16x8_offset8(kw[kb])), qa[kb], sacc, 0, 0, 0);
-          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale
-          const float4 ks = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
-          sacc[0] = (sacc[0] - q8[0]) * ks.x;
-          sacc[1] = (sacc[1] - q8[0]) * ks.y;
-          sacc[2] = (sacc[2] - q8[0]) * ks.z;
-          sacc[3] = (sacc[3] - q8[0]) * ks.w;
-        } else {
+        } else if constexpr (kFp8) {
 #pragma unroll
           for (int kb = 0; kb < kKBlocks; ++kb) {
-            const uint4 kw = k_group(ktile, 16 * tg + n, 4 * kb + grp);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
+            const uint2 w = *reinterpret_cast<const uint2*>(
+                ktile + k_tile_offset<kRowBytes>(16 * tg + n, (4 * kb + grp) >> 1) +
+                8 * ((4 * kb + grp) & 1));
+            kraw[tg][kb].x = w.x;
+            kraw[tg][kb].y = w.y;
           }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < kKBlocks; ++kb)
+            kraw[tg][kb] = *reinterpret_cast<const uint4*>(
+                ktile + k_tile_offset<kRowBytes>(16 * tg + n, 4 * kb + grp));
+        }
+      }
+      // V, read column-wise with the transposing LDS reads.
+      //   bf16: column block nb of 16 dims; lane 4q+u of the group gets
+      //     element e from lane 4e+q, which addresses row 4*grp + e (+16 for
+      //     slots 4..7), dims 16*nb + 4q .. +3.
+      //   E4M3: column block nb of 16 dims; lane 8q+u of the group gets byte e
+      //     from lane 2e+q, which addresses row 16*(e/4) + 4*grp + e%4,
+      //     bytes 16*nb + 8q .. +7.
+      //   INT4: column block cb of 32 dims; lane 8q+u of the group gets byte e
+      //     from lane 2e+q, which addresses row 16*(e/4) + 4*grp + e%4, bytes
+      //     16*cb + 8q .. +7; so byte e holds row e's dims 32*cb + 16q + 2u
+      //     (low nibble) and + 1 (high nibble): one column of each of two
+      //     MFMAs.
+      constexpr int kVBlocks = kInt4 ? D / 32 : kNBlocks;
+      uint4 vraw[kVBlocks];
+#pragma unroll
+      for (int nb = 0; nb < kVBlocks; ++nb) {
+        if constexpr (kInt4 || kFp8) {
+          const int e = n >> 1;
+          const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
+          const uint2 w = lds_read_tr8(vtile + k_tile_offset<kRowBytes>(row, nb) + 8 * (lane & 1));
+          vraw[nb] = make_uint4(w.x, w.y, 0u, 0u);
+        } else {
+          const int row = 4 * grp + (n >> 2);
+          const int c = 2 * nb + ((lane & 3) >> 1);
+          const uint2 w0 =
+              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row, c) + 8 * (lane & 1));
+          const uint2 w1 =
+              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row + 16, c) + 8 * (lane & 1));
+          vraw[nb] = make_uint4(w0.x, w0.y, w1.x, w1.y);
+        }
+      }
+      float4 ksc[2], vsc[2];   // INT4 row scales of this lane's rows
+      if constexpr (kInt4) {
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg) {
+          ksc[tg] = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
+          vsc[tg] = *reinterpret_cast<const float4*>(sct + kT + 16 * tg + 4 * grp);
+        }
+      }
+
+      // S^T = K q^T: lane l gets the logits of head n for rows 16*tg + 4*grp + r
+      // (rows at or past row_end are masked, which only a split's last tile
+      // can hold)
+      const bool full = r0 + kT <= row_end;
+      float x[2][4];
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < kKBlocks; ++kb) {
+          uint4 kw;
+          if constexpr (kInt4)
+            kw = int4x8_to_bf16x8_offset8(kraw[tg][kb].x);
+          else if constexpr (kFp8)
+            kw = e4m3x8_to_bf16x8(make_uint2(kraw[tg][kb].x, kraw[tg][kb].y));
+          else
+            kw = kraw[tg][kb];
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
+        }
+        if constexpr (kInt4) {
+          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale
+          sacc[0] = (sacc[0] - q8[0]) * ksc[tg].x;
+          sacc[1] = (sacc[1] - q8[0]) * ksc[tg].y;
+          sacc[2] = (sacc[2] - q8[0]) * ksc[tg].z;
+          sacc[3] = (sacc[3] - q8[0]) * ksc[tg].w;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          x[tg][r] = (r0 + 16 * tg + 4 * grp + r < row_end) ? sacc[r] * c2 : -INFINITY;
+          x[tg][r] = (full || r0 + 16 * tg + 4 * grp + r < row_end) ? sacc[r] * c2 : -INFINITY;
       }
       // tile max of head n over the four lanes that hold it (row r0 is always
       // valid, so the max is finite)
@@ -717,28 +782,18 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       }
       if constexpr (kInt4) {
         // p times the row's V scale (rows past the sequence have scale 0 and p 0)
-        const float4 v0 = *reinterpret_cast<const float4*>(sct + kT + 4 * grp);
-        const float4 v1 = *reinterpret_cast<const float4*>(sct + kT + 16 + 4 * grp);
-        pv[0] *= v0.x; pv[1] *= v0.y; pv[2] *= v0.z; pv[3] *= v0.w;
-        pv[4] *= v1.x; pv[5] *= v1.y; pv[6] *= v1.z; pv[7] *= v1.w;
+        pv[0] *= vsc[0].x; pv[1] *= vsc[0].y; pv[2] *= vsc[0].z; pv[3] *= vsc[0].w;
+        pv[4] *= vsc[1].x; pv[5] *= vsc[1].y; pv[6] *= vsc[1].z; pv[7] *= vsc[1].w;
       }
       bf16x8_t ph, pl;
       split_bf16x8(pv, ph, pl);
       // ---- p.V on the matrix cores ----
       if constexpr (kInt4) {
-        // V^T column blocks of 32 dims: lane 8q+u of the group gets byte e
-        // from lane 2e+q, which addresses row 16*(e/4) + 4*grp + e%4, bytes
-        // 16*cb + 8q .. +7; so byte e holds row e's dims 32*cb + 16q + 2u
-        // (low nibble) and + 1 (high nibble): one column of each of two
-        // MFMAs.  The offset 8 of the codes comes off at the end through
-        // osum, the same products against a column of ones.
-        const int e = n >> 1;
-        const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
+        // The offset 8 of the codes comes off at the end through osum, the
+        // same products against a column of ones.
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
-          const uint2 w =
-              lds_read_tr8(vtile + k_tile_offset<kRowBytes>(row, cb) + 8 * (lane & 1));
-          const uint32_t x0 = w.x ^ 0x88888888u, x1 = w.y ^ 0x88888888u;
+          const uint32_t x0 = vraw[cb].x ^ 0x88888888u, x1 = vraw[cb].y ^ 0x88888888u;
           const uint4 vlo = e4m3x8_to_bf16x8(make_uint2(x0 & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu), 512.0f);
           const uint4 vhi = e4m3x8_to_bf16x8(
               make_uint2((x0 >> 4) & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu), 512.0f);
@@ -754,28 +809,10 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
         osum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(one4), osum, 0, 0, 0);
         return;
       }
-      // V^T column blocks of 16 dims
 #pragma unroll
       for (int nb = 0; nb < kNBlocks; ++nb) {
-        uint4 vw;
-        if constexpr (kFp8) {
-          // lane 8q+u of the group gets byte e from lane 2e+q: lane 2e+q
-          // addresses row 16*(e/4) + 4*grp + e%4, bytes 16*nb + 8q .. +7
-          const int e = n >> 1;
-          const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
-          vw = e4m3x8_to_bf16x8(
-              lds_read_tr8(vtile + k_tile_offset<kRowBytes>(row, nb) + 8 * (lane & 1)));
-        } else {
-          // lane 4q+u of the group gets element e from lane 4e+q: lane 4e+q
-          // addresses row 4*grp + e (+16 for slots 4..7), dims 16*nb + 4q .. +3
-          const int row = 4 * grp + (n >> 2);
-          const int c = 2 * nb + ((lane & 3) >> 1);
-          const uint2 w0 =
-              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row, c) + 8 * (lane & 1));
-          const uint2 w1 =
-              lds_read_tr16(vtile + k_tile_offset<kRowBytes>(row + 16, c) + 8 * (lane & 1));
-          vw = make_uint4(w0.x, w0.y, w1.x, w1.y);
-        }
+        const uint4 vw =
+            kFp8 ? e4m3x8_to_bf16x8(make_uint2(vraw[nb].x, vraw[nb].y)) : vraw[nb];
         oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vw), oacc[nb], 0, 0, 0);
         oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vw), oacc[nb], 0, 0, 0);
       }
