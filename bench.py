@@ -55,6 +55,9 @@ def parse():
                     help="page size in rows: time the paged entry point over a shuffled pool")
     ap.add_argument("--paged-layout", choices=("hnd", "nhd"), default="hnd")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate; 0 = auto")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the calls replayed from one HIP graph (reported beside, "
+                         "never as, the value)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline; 0 skips it")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -226,19 +229,21 @@ def main():
     # One prepared decode-attention call per K/V copy.  It is a single kernel
     # launch: phase 1 plus the fused phase-2 merge by the last workgroup of
     # each (b, kv-head).
-    if paged is not None:
-        calls = [das.prepare_decode_paged(q, ks[c], vs[c], table, sl, x.scale, paged.page_size,
-                                          paged.layout, out, lse, args.splits, ws,
-                                          k_scale=k_scale, v_scale=v_scale)
-                 for c in range(copies)]
-    elif quant:
-        name = "das_decode_attention_int4" if int4 else "das_decode_attention_fp8"
-        calls = [das.prepare_decode(name, q, ks[c], vs[c], sl, x.scale, out, lse, args.splits, ws,
-                                    k_scale=kss[c], v_scale=vss[c])
-                 for c in range(copies)]
-    else:
-        calls = [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
-                                    args.splits, ws) for c in range(copies)]
+    def make_calls(stream=None):
+        if paged is not None:
+            return [das.prepare_decode_paged(q, ks[c], vs[c], table, sl, x.scale, paged.page_size,
+                                             paged.layout, out, lse, args.splits, ws, stream=stream,
+                                             k_scale=k_scale, v_scale=v_scale)
+                    for c in range(copies)]
+        if quant:
+            name = "das_decode_attention_int4" if int4 else "das_decode_attention_fp8"
+            return [das.prepare_decode(name, q, ks[c], vs[c], sl, x.scale, out, lse, args.splits,
+                                       ws, stream=stream, k_scale=kss[c], v_scale=vss[c])
+                    for c in range(copies)]
+        return [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
+                                   args.splits, ws, stream=stream) for c in range(copies)]
+
+    calls = make_calls()
 
     for i in range(args.warmup):
         calls[i % copies]()
@@ -260,6 +265,29 @@ def main():
     ms_per_step = elapsed / K * 1e3
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (kernel_ms * 1e-3) / 1e9
+
+    # For reference only (not `value`): the same K calls captured in one HIP
+    # graph and replayed, as a serving engine issues a decode step.  The
+    # library allocates and synchronises nothing, so its calls capture as is.
+    graph_us = None
+    if args.graph:
+        gs = torch.cuda.Stream()
+        gcalls = make_calls(gs)
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=gs):
+            for i in range(K):
+                gcalls[i % copies]()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = round(g0.elapsed_time(g1) / K * 1e3, 2)
+        del graph
 
     result = {
         "metric": METRIC,
@@ -288,6 +316,7 @@ def main():
                       if paged is not None else None),
             "kv_copies_rotated": copies,
             "us_per_call": round(ms_per_step * 1e3, 2),
+            "us_per_call_graph_replay": graph_us,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         },
         "roofline": {
