@@ -746,8 +746,14 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
           sacc[3] = (sacc[3] - q8[0]) * ksc[tg].w;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[tg][r] = (full || r0 + 16 * tg + 4 * grp + r < row_end) ? sacc[r] * c2 : -INFINITY;
+        for (int r = 0; r < 4; ++r) x[tg][r] = sacc[r] * c2;
+      }
+      if (!full) {
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r0 + 16 * tg + 4 * grp + r >= row_end) x[tg][r] = -INFINITY;
       }
       // tile max of head n over the four lanes that hold it (row r0 is always
       // valid, so the max is finite)
