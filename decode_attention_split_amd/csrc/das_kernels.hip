@@ -760,21 +760,17 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
       float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
       mt = reduce_lane_bits<4, true>(mt);
-      const float mn = fmaxf(m_lane, mt);
-      const float alpha = fast_exp2(m_lane - mn);
-      const bool grow = __builtin_amdgcn_ballot_w64(mn > m_lane) != 0;
-      m_lane = mn;
-      // p in the A operand's k-slot order: slot i of lane group grp is row
-      // 16*(i/4) + 4*grp + i%4 (the V operand below uses the same order)
-      float pv[8];
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(x[i / 4][i % 4] - mn);
-        lsum += pv[i];
-      }
-      l_sum = fmaf(l_sum, alpha, lsum);
-      if (grow) {
+      // Lazy rescaling: the running max moves only when a tile's max exceeds
+      // it by more than kLazyLog2 (base-2 units).  Until then p = exp2(x - m)
+      // stays below 2^kLazyLog2, which the fp32 sums and the hi/lo bf16 split
+      // of p carry without loss, and the accumulators need no rescaling; the
+      // final division and the LSE use the same m, so the result changes only
+      // by rounding.  The first tile always moves it (m starts at -inf).
+      constexpr float kLazyLog2 = 8.f;
+      if (__builtin_amdgcn_ballot_w64(mt > m_lane + kLazyLog2) != 0) {
+        const float mn = fmaxf(m_lane, mt);
+        const float alpha = fast_exp2(m_lane - mn);   // 0 on the first tile
+        l_sum *= alpha;
         // row r of this lane's accumulators is head 4*grp + r, whose factor
         // the lane with n = 4*grp + r holds (G = 4: heads 0..3 in group 0)
 #pragma unroll
@@ -785,7 +781,18 @@ __global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
           for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb][r] *= f;
           if constexpr (kInt4) osum[r] *= f;
         }
+        m_lane = mn;
       }
+      // p in the A operand's k-slot order: slot i of lane group grp is row
+      // 16*(i/4) + 4*grp + i%4 (the V operand below uses the same order)
+      float pv[8];
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = fast_exp2(x[i / 4][i % 4] - m_lane);
+        lsum += pv[i];
+      }
+      l_sum += lsum;
       if constexpr (kInt4) {
         // p times the row's V scale (rows past the sequence have scale 0 and p 0)
         pv[0] *= vsc[0].x; pv[1] *= vsc[0].y; pv[2] *= vsc[0].z; pv[3] *= vsc[0].w;
