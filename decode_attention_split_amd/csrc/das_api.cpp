@@ -40,6 +40,9 @@ constexpr int64_t kMinSplitsLongest = 5;
 // das_decode_attention fuses the merge into phase 1 up to this many split
 // workgroups per CU (see das_decode_attention below).
 constexpr int64_t kFusedWgsPerCu = 4;
+// Phase-1 workgroups are spread one per CU unless the grid holds at least
+// this many per CU (see run_phase1).
+constexpr int64_t kSpreadWgsPerCu = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t q) { return ceil_div(a, q) * q; }
@@ -237,8 +240,14 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   // on some CUs while others idle whenever fewer workgroups stream than the
   // chip holds -- a small grid, or a varlen batch whose empty splits exit at
   // once (the ragged G=8 batch on an E4M3 cache: 103 us doubled up, 73 us
-  // spread).
-  const bool one_per_cu = DAS_ONE_PER_CU != 0;
+  // spread).  A grid of many workgroups per CU is left to the dispatcher:
+  // kernels whose registers and LDS allow two workgroups on a CU (the INT4
+  // matrix-core path) then hide each other's stalls (INT4 varlen B=64
+  // decode, 2560 workgroups: 158 us one per CU, 142 us two).
+  int cus = 0;
+  if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
+  const bool one_per_cu =
+      DAS_ONE_PER_CU != 0 && (int64_t)B * Hkv * c.ns < kSpreadWgsPerCu * (int64_t)cus;
   return das::launch_split_kv_decode(D, c.G, kv.format, kv.paged(), B, a, one_per_cu, st) ==
                  hipSuccess
              ? DAS_OK

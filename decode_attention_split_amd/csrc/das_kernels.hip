@@ -331,8 +331,17 @@ constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
 // §6); a tile never straddles a page (pages are >= 32 rows, chunks whole
 // pages), so every tile finds its page with one table entry.
 // ---------------------------------------------------------------------------
+// Waves per SIMD the register allocator must allow.  The INT4 kernels with
+// G = 4 fit four (128 registers, no spills) and are bound by their per-row
+// work, so two of their workgroups on a CU hide each other's stalls; the
+// others keep two (their tiles or registers leave room for one workgroup).
+template <int G, int kKv>
+constexpr int min_waves_per_eu() {
+  return (kKv == kKvInt4 && G == 4) ? 4 : DAS_MIN_WAVES_PER_EU;
+}
+
 template <int D, int G, int kKv, bool kPaged>
-__global__ __launch_bounds__(kThreads, DAS_MIN_WAVES_PER_EU)
+__global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     void split_kv_decode_kernel(SplitArgs a) {
   constexpr bool kFp8 = kKv == kKvE4m3;
   constexpr bool kInt4 = kKv == kKvInt4;
