@@ -91,5 +91,25 @@ def test_named_config_full_size(idx):
     d_l = float(torch.max(torch.abs(lse1 - lse)))
     note(f"  split invariance: max|out diff| {d_o:.2e}, max|lse diff| {d_l:.2e}")
     assert d_o <= 5e-4 and d_l <= 1e-4
+    note(f"case full config {cfg.name}: bf16 output")
+    outb, lseb = run(x, 0, out_dtype=torch.bfloat16, tensors=t)
+    check_bf16(outb, ref[0], f"{cfg.name} bf16 auto")
+    assert float(np.max(np.abs(lseb.cpu().numpy() - ref[1]))) <= 1e-4
     del t
     torch.cuda.empty_cache()
+
+
+def test_many_forced_splits_and_empty_ones():
+    """Forced split counts far above the automatic plan (64 and more, chunks
+    down to the 128-row quantum) on a batch whose short sequences leave most
+    splits empty, against the oracle."""
+    lens = (16384, 9000, 300, 129, 1, 0)
+    cfg = workloads.custom_config(len(lens), 32, 8, 128, 16384)
+    x = workloads.make_inputs(cfg, 4100, seq_lens=lens)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    for ns in (64, 100, 128):
+        got_ns, chunk = das.das_plan(len(lens), 8, 4, 16384, 128, ns)
+        note(f"case forced splits {ns}: plan ns={got_ns} chunk={chunk}")
+        out, lse = run(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"forced ns={ns}")
