@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoads = kT / kRowsPerLoad;  // V loads per lane per tile
   constexpr int kVLaneBytes = kRowBytes / kLanesPerRow;
-  // K: 16-byte loads straight into LDS, kKLanesPerRow lanes per row.
+  // K (and, G >= 4, V) tiles: 16-byte loads, kKLanesPerRow lanes per row.
   constexpr int kKLanesPerRow = kRowBytes / 16;
   constexpr int kKRowsPerLoad = 64 / kKLanesPerRow;
   constexpr int kKLoads = kT / kKRowsPerLoad;
@@ -573,10 +573,11 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   };
 
   // G >= 4: the tiles go through registers, one tile ahead of the one being
-  // processed.  fetch_tile loads tile r0 -- what the LDS-direct loads of
-  // load_tile would write at [m KiB + 16 lane] of the K and V tiles, and the
-  // INT4 row scales (lanes 0..kT-1 K, kT..63 V) -- and stage_tile writes it
-  // into the wave's LDS tiles once the previous tile has been processed.
+  // processed.  fetch_tile loads tile r0 -- the 16-byte chunks that go to
+  // [m KiB + 16 lane] of the K and V tiles (the layout load_tile's K loads
+  // produce), and the INT4 row scales (lanes 0..kT-1 K, kT..63 V) -- and
+  // stage_tile writes it into the wave's LDS tiles once the previous tile
+  // has been processed.
   // The next tile's loads are thus in flight while the current one is
   // processed, instead of the wave issuing nothing during that time.
   struct TileRegs {
