@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8", "int4"), default="bf16",
-                    help="K/V cache element: bf16, or E4M3 codes with per-kv-head scales")
+                    help="K/V cache element: bf16, E4M3 codes with per-kv-head scales, or "
+                         "INT4 codes with per-row scales")
     ap.add_argument("--paged", type=int, default=0,
                     help="page size in rows: time the paged entry point over a shuffled pool")
     ap.add_argument("--paged-layout", choices=("hnd", "nhd"), default="hnd")
