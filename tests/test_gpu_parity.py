@@ -113,3 +113,52 @@ def test_many_forced_splits_and_empty_ones():
         note(f"case forced splits {ns}: plan ns={got_ns} chunk={chunk}")
         out, lse = run(x, ns, tensors=t)
         check_f32(out, lse, *ref, f"forced ns={ns}")
+
+
+def _steer_keys(x, ramps):
+    """Give every (batch row, kv-head) a designed logit profile along the
+    sequence: valid row j of K becomes a quarter of its random value plus
+    ramps[b][j] / scale times q0 / |q0|^2 (q0 the group's first query head),
+    rounded to bf16.  Head q0 then sees logits close to ramps[b][j] (natural
+    log units); the group's other heads see small multiples of it.  Rows past
+    the sequence keep their NaN marker."""
+    B, Hkv, _, D = x.k.shape
+    G = x.q.shape[1] // Hkv
+    q = workloads.bf16_bits_to_f32(x.q).astype(np.float64)
+    bits = x.k.copy()
+    for b in range(B):
+        L = int(x.seq_lens[b])
+        for g in range(Hkv):
+            u = q[b, g * G]
+            k = workloads.bf16_bits_to_f32(x.k[b, g, :L]).astype(np.float64) * 0.25
+            k += np.outer(np.asarray(ramps[b][:L]) / x.scale, u / np.dot(u, u))
+            bits[b, g, :L] = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    x.k = bits
+    return x
+
+
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (64, 4)],
+                         ids=lambda v: str(v))
+def test_rising_falling_and_spiking_logits(D, G):
+    """Logit profiles that move the running max in every way the online
+    softmax meets (random keys hardly do): a slow rise over the whole
+    sequence (the max grows a little in every tile, so rescaling waits for
+    many tiles and the weights p reach the largest values the kernel lets
+    them grow to), a sawtooth rising 5.5 per 32-row tile and dropping back
+    every 12 tiles, a single late spike 30 above the rest, and a slow fall
+    (the first tile holds the max throughout)."""
+    lens = (3000, 2000, 2500, 1500)
+    j = np.arange(3000, dtype=np.float64)
+    spike = np.zeros(3000)
+    spike[2500 - 5:2500] = 30.0
+    ramps = [0.02 * j, 5.5 * ((j // 32) % 12), spike, -0.02 * j]
+    cfg = workloads.custom_config(len(lens), 2 * G, 2, D, 3000)
+    x = _steer_keys(workloads.make_inputs(cfg, 4200 + D + G, seq_lens=lens), ramps)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    # the profiles did steer the logits: the spike sequence's LSE sits near 30
+    assert np.all(ref[1][2, ::G] > 25.0)
+    t = upload(x)
+    for ns in (0, 1, 3, 8):
+        note(f"case steered logits D={D} G={G} num_splits={ns}")
+        out, lse = run(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"steered D={D} G={G} ns={ns}")
