@@ -13,8 +13,14 @@ import workloads
 
 OUT_TOL = 5e-4      # fp32-output mode: max |err| on the output
 LSE_TOL = 1e-4      # max |err| on the natural-log LSE
-BF16_FLOOR = 2.0 ** -12   # below this |oracle| the bf16 check is absolute
-BF16_ABS = 2.0 ** -19     # bf16 ulp at 2^-12
+# bf16 output: ordinal distance <= 1 from the oracle rounded to bf16 where
+# |oracle| >= BF16_FLOOR * S, and |err| <= BF16_ABS * S below that, with
+# S = max(1, max |oracle|) over the call's output.  An exact fp32 pipeline
+# leaves an absolute cancellation error at the scale of the values it
+# averages, so the ulp test means something only down to a floor that grows
+# with that scale.
+BF16_FLOOR = 2.0 ** -12
+BF16_ABS = 2.0 ** -19     # the bf16 ulp at 2^-12
 
 
 def note(msg: str) -> None:
@@ -71,10 +77,12 @@ def check_bf16(out: torch.Tensor, ref_o: np.ndarray, what: str):
     want_bits = oracle.bf16_bits_of(want)
     dist = np.abs(bf16_ordinal(got_bits) - bf16_ordinal(want_bits))
     got = workloads.bf16_bits_to_f32(got_bits).astype(np.float64)
-    big = np.abs(ref_o) >= BF16_FLOOR
+    S = max(1.0, float(np.max(np.abs(ref_o)))) if ref_o.size else 1.0
+    big = np.abs(ref_o) >= BF16_FLOOR * S
     literal = int(np.count_nonzero(dist > 1))
     worst_small = float(np.max(np.abs(got - ref_o)[~big])) if (~big).any() else 0.0
-    note(f"  {what}: bf16 max ulp (|ref|>=2^-12) {int(dist[big].max()) if big.any() else 0}, "
+    note(f"  {what}: bf16 max ulp (|ref|>=2^-12*S, S={S:.3g}) {int(dist[big].max()) if big.any() else 0}, "
          f"elements >1 ulp anywhere {literal} of {dist.size}, worst |err| below floor {worst_small:.2e}")
     assert np.all(dist[big] <= 1), f"{what}: bf16 output more than 1 ulp from the rounded oracle"
-    assert worst_small <= BF16_ABS, f"{what}: near-zero bf16 error {worst_small:.2e} > 2^-19"
+    assert worst_small <= BF16_ABS * S, \
+        f"{what}: near-zero bf16 error {worst_small:.2e} > 2^-19 * {S:.3g}"

@@ -3,9 +3,9 @@ FP8): the HIP path vs the fp64 oracle, element by element, on seeded inputs.
 Codes are two's-complement nibbles (element 2i in the low nibble), one fp32
 scale per cached row for K and one for V.  Same tolerances as the bf16 cache:
 fp32 output max|err| <= 5e-4, LSE max|err| <= 1e-4; bf16 output within 1 bf16
-ulp of the rounded oracle where |oracle| >= 2^-12.  Rows past seq_lens hold
-code byte 0x88 and a NaN scale in every cache, so a read past a sequence shows
-up as a wrong or non-finite result."""
+ulp of the rounded oracle where |oracle| >= 2^-12 * S, S = max(1, max
+|oracle|).  Rows past seq_lens hold code byte 0x88 and a NaN scale in every
+cache, so a read past a sequence shows up as a wrong or non-finite result."""
 import numpy as np
 import pytest
 import torch
