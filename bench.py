@@ -139,8 +139,23 @@ def cpu_baseline(x, target_s: float):
     gbs = sample_bytes * calls / el / 1e9
     sample = (f"{calls} oracle call(s) over {rows} of {B} batch row(s) "
               f"({sample_bytes / 1e6:.1f} MB of K+V per call) in {el:.1f} s")
+    # the same sample on one thread, for a quarter of the time (at least one call)
+    oracle.set_threads(1)
+    try:
+        calls1 = 0
+        t1 = time.perf_counter()
+        while True:
+            oracle.attention(q, k, v, sl, x.scale)
+            calls1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= target_s / 4 or calls1 >= 1000:
+                break
+    finally:
+        oracle.set_threads(threads)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": sample, "us_per_call": round(el / calls * 1e6 * B / rows, 1),
+            "one_thread": {"value": round(sample_bytes * calls1 / el1 / 1e9, 4), "unit": "GB/s",
+                           "calls": calls1, "seconds": round(el1, 1)},
             "cpu": cpu_model()}
 
 
