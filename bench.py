@@ -56,6 +56,9 @@ def parse():
                     help="page size in rows: time the paged entry point over a shuffled pool")
     ap.add_argument("--paged-layout", choices=("hnd", "nhd"), default="hnd")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies to rotate; 0 = auto")
+    ap.add_argument("--isolated", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time 100 calls one by one, each after a 1 GiB cache flush and "
+                         "between its own events (median; reported beside, never as, the value)")
     ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the calls replayed from one HIP graph (reported beside, "
                          "never as, the value)")
@@ -305,6 +308,25 @@ def main():
         graph_us = round(g0.elapsed_time(g1) / K * 1e3, 2)
         del graph
 
+    # Also for reference: calls one at a time, each after a 1 GiB write that
+    # evicts the cache (4x the 256 MB Infinity Cache) and between its own
+    # pair of events; the median of 100.
+    isolated_us = None
+    if args.isolated:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        n = 100
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            flush.fill_(i & 255)
+            evs[i][0].record()
+            calls[i % copies]()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        isolated_us = round(sorted(a.elapsed_time(b) for a, b in evs)[n // 2] * 1e3, 2)
+        del flush
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -333,6 +355,7 @@ def main():
             "kv_copies_rotated": copies,
             "us_per_call": round(ms_per_step * 1e3, 2),
             "us_per_call_graph_replay": graph_us,
+            "us_per_call_isolated_median": isolated_us,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         },
         "roofline": {
