@@ -205,6 +205,7 @@ def main():
         Smax = paged.block_table.shape[1] * paged.page_size
     kv_code = das.DAS_INT4 if int4 else (das.DAS_E4M3 if fp8 else das.DAS_BF16)
     ns, chunk = das.das_plan_kv(kv_code, B, Hkv, Hq // Hkv, Smax, D, args.splits)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     if paged is not None and chunk % paged.page_size:
         chunk = -(-chunk // paged.page_size) * paged.page_size
         ns = -(-Smax // chunk)
@@ -360,7 +361,10 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_kv_decode",
+            # phase 2 runs fused unless the plan has more than 4 split
+            # workgroups per CU or more (b, kv-head) pairs than counter slots
+            "kernel": ("split_kv_decode" if B * Hkv <= 65536 and B * Hkv * ns <= 4 * cus
+                       else "split_kv_decode + lse_combine"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

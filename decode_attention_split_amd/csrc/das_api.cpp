@@ -25,12 +25,13 @@ std::atomic<int> g_cu_cache[kMaxDevices];
 // 8-wave phase-1 workgroup is resident per CU.  Measured on MI355X, about
 // three streaming workgroups per four CUs already saturate HBM, and the
 // fewer, longer splits cut the partial results and the per-workgroup start
-// and end latencies (32K-row GQA decode: 24 splits 28.5 us, 32 splits 30.7 us).
+// and end latencies (32K-row GQA decode: 16 splits 27.6 us, 24 splits
+// 25.3 us, 32 splits 25.7 us).
 constexpr int64_t kTargetWgsPer4Cus = 3;
 // An INT4 cache moves a quarter of the bytes per row, so its call is bound
 // by the per-row work on the CUs rather than by HBM, and the fused call aims
-// for one workgroup on every CU (128K-row GQA decode: 24 splits 44.3 us, 32
-// splits 35.0 us; an E4M3 cache measured the same with either plan).
+// for one workgroup on every CU (128K-row GQA decode: 24 splits 39 us, 32
+// splits 33-37 us; an E4M3 cache measured the same with either plan).
 constexpr int64_t kTargetWgsPer4CusInt4 = 4;
 constexpr int64_t kMaxChunk = 8192;
 // Even when the batch alone fills the chip, a maximal-length sequence is cut
@@ -238,12 +239,14 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   a.out_bf16 = out_dtype == DAS_BF16;
   // One workgroup per CU: left to itself the dispatcher doubles workgroups up
   // on some CUs while others idle whenever fewer workgroups stream than the
-  // chip holds -- a small grid, or a varlen batch whose empty splits exit at
-  // once (the ragged G=8 batch on an E4M3 cache: 103 us doubled up, 73 us
-  // spread).  A grid of many workgroups per CU is left to the dispatcher:
-  // kernels whose registers and LDS allow two workgroups on a CU (the INT4
-  // matrix-core path) then hide each other's stalls (INT4 varlen B=64
-  // decode, 2560 workgroups: 158 us one per CU, 142 us two).
+  // chip holds (INT4 cache, one workgroup per CU against doubled up: 32K-row
+  // GQA decode 15.3 against 18.6 us, 128K 35 against 46 us).  A grid of
+  // many workgroups per CU is left to the dispatcher: kernels whose
+  // registers and LDS allow two workgroups on a CU (the INT4 matrix-core
+  // path) then hide each other's stalls (INT4 varlen B=64 decode, 2560
+  // workgroups: 153 us one per CU, 135 us two).  The bf16 kernels with
+  // G >= 4 hold more than half a CU's LDS, so they are spread anyway; the
+  // E4M3 kernels measure the same either way.
   int cus = 0;
   if (device_cus(0, &cus) != DAS_OK) return DAS_ELAUNCH;
   const bool one_per_cu =
@@ -301,7 +304,7 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
   // Every split workgroup then ends with a store-completion wait and a
   // counter round trip while it holds its CU; with many more workgroups than
   // CUs that costs more than a second, small merge kernel (B=64 varlen
-  // decode, 2560 workgroups: 375 us fused, 363 us as two kernels), so the
+  // decode, 2560 workgroups: 375 us fused, 359 us as two kernels), so the
   // merge is fused only up to kFusedWgsPerCu workgroups per CU.  Shapes with
   // more (b, kv-head) pairs than counter slots always use the second kernel.
   int cus = 0;

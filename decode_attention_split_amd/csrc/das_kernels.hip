@@ -20,12 +20,12 @@
 //     lane ends up holding one head's logits for eight rows -- exactly its
 //     slots of the A operand of p.V, with no data movement.  p is split into
 //     two bf16 halves (p = hi + lo to about 2^-18 relative), so p.V keeps
-//     fp32-level accuracy; V is exact in bf16 (and so is E4M3).  K and V go
-//     through a per-wave LDS tile with an XOR swizzle, staged from registers
-//     one tile ahead (a wave's next tile is in flight while it processes the
-//     current one); K is read one row per lane, V column-wise with the
-//     gfx950 transposing LDS reads (ds_read_b64_tr_b16 / _tr_b8), both free
-//     of bank conflicts.
+//     fp32-level accuracy; V is exact in bf16 (and so are E4M3 and the INT4
+//     codes).  K and V go through a per-wave LDS tile with an XOR swizzle,
+//     staged from registers one tile ahead (a wave's next tile is in flight
+//     while it processes the current one); K is read one row per lane, V
+//     column-wise with the gfx950 transposing LDS reads
+//     (ds_read_b64_tr_b16 / _tr_b8).
 //   * For G in {1, 2} q.K^T is a matrix-vector product on the vector ALUs
 //     (v_dot2_f32_bf16: exact bf16 products, fp32 accumulation), and p.V runs
 //     on the vector ALUs in fp32 straight from the coalesced V registers; p
@@ -33,10 +33,13 @@
 //     goes from HBM straight into the LDS tile (buffer_load ... lds).
 //   * The online softmax keeps, per wave and head, a running max (base-2
 //     units: logits are scaled by scale*log2(e) in fp32 after the dot) and
-//     rescales the partial sums only when the max grows.
+//     rescales the partial sums only when the max grows (on the matrix-core
+//     path, only when it grows by more than 2^8).
 //   * The waves of a workgroup merge their states through LDS at the end;
 //     the workgroup then writes its split's (o, m, l) partial, or, for a
-//     single-split plan, the final output.
+//     sequence with a single split, the final output.  With the fused
+//     phase 2 the last workgroup of each (batch row, kv-head) to finish
+//     merges that pair's partials in the same launch.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -270,6 +273,8 @@ constexpr int vmcnt_imm(int n) {
   return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// Orders this wave's LDS accesses before the point against those after it
+// (each wave owns its tile region, so no workgroup barrier is needed).
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
