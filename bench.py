@@ -2,15 +2,18 @@
 
 One step = one decode-attention call (das_decode_attention: phase 1 with
 the phase-2 merge fused into the last workgroup of each (batch row,
-kv-head), a single kernel launch) over the synthetic workload, with every
-input already resident in HBM.  K/V are rotated over several copies so that repeated steps read
-from HBM rather than from the 256 MB last-level cache.
+kv-head), a single kernel launch; on grids of more than 4 split workgroups
+per CU phase 2 runs as a second, small kernel) over the synthetic workload,
+with every input already resident in HBM.  K/V are rotated over several
+copies so that repeated steps read from HBM rather than from the 256 MB
+last-level cache.
 
-Prints one JSON line on stdout.  Also reports, for the dominant (and only)
-kernel, the achieved algorithmic HBM bandwidth against the MI355X peak,
-measured with HIP events on the launch stream around the timed launches,
-and the fp64 CPU oracle's throughput on a bounded sample of the same
-workload (the reported CPU baseline).
+Prints one JSON line on stdout.  Also reports the achieved algorithmic HBM
+bandwidth of the call's kernels against the MI355X peak, measured with HIP
+events on the launch stream around the timed launches; for reference only,
+the same calls replayed from one HIP graph and the median of calls issued
+one at a time after a cache flush; and the fp64 CPU oracle's throughput on a
+bounded sample of the same workload (the reported CPU baseline).
 """
 from __future__ import annotations
 
