@@ -186,16 +186,24 @@ __device__ __forceinline__ void e4m3x8_to_f32(uint2 w, float* f) {
 // is taken off by the caller (by linearity, once per dot product or sum).
 // The eight codes of one dword w (elements 0..7, element 2i in the low
 // nibble of byte i), as bf16 values u in the order 0, 2, 4, 6, 1, 3, 5, 7.
+// The codes u of the low nibbles (even elements) and of the high nibbles
+// (odd elements) of a dword, one per byte.  Masking before flipping the top
+// bit makes each a single three-input bit operation (after a shift for the
+// high nibbles).
+__device__ __forceinline__ uint32_t int4_low_offset8(uint32_t w) {
+  return (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+}
+__device__ __forceinline__ uint32_t int4_high_offset8(uint32_t w) {
+  return ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+}
 __device__ __forceinline__ uint4 int4x8_to_bf16x8_offset8(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  return e4m3x8_to_bf16x8(make_uint2(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu), 512.0f);
+  return e4m3x8_to_bf16x8(make_uint2(int4_low_offset8(w), int4_high_offset8(w)), 512.0f);
 }
 
 // The eight codes of one dword as fp32 n * 2^-9, in element order (exact:
 // u * 2^-9 from the converter minus 8 * 2^-9).
 __device__ __forceinline__ void int4x8_to_f32_scaled(uint32_t w, float* f) {
-  const uint32_t x = w ^ 0x88888888u;
-  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const uint32_t lo = int4_low_offset8(w), hi = int4_high_offset8(w);
   const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
   const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
   const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -631,7 +639,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
 #pragma unroll
     for (int m = 0; m < kKLoads; ++m)
       *reinterpret_cast<uint4*>(kbuf + kKTileBytes + m * 1024 + 16 * lane) = t.v[m];
-    if constexpr (kInt4) reinterpret_cast<float*>(kbuf + 2 * kKTileBytes)[lane] = t.sc;
+    // INT4: the K row scales go in with the logit scale folded in
+    if constexpr (kInt4)
+      reinterpret_cast<float*>(kbuf + 2 * kKTileBytes)[lane] = lane < kT ? t.sc * c2 : t.sc;
     wave_lds_fence();
   };
 
@@ -654,11 +664,14 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   auto process_tile = [&](int r0, const VReg* vr, const unsigned char* ktile) {
     if constexpr (kMfmaPv) {
       // K and V are in LDS (staged by stage_tile).  Every LDS read of the
-      // tile is issued first, so their latency overlaps the q.K^T products
-      // and the softmax instead of stalling each product in turn.
+      // tile's K and V is issued first, so their latency overlaps the q.K^T
+      // products and the softmax instead of stalling each product in turn.
+      // The INT4 row scales are read where they are used: they are few, and
+      // holding them from the start would take registers those kernels lack.
       const unsigned char* vtile = ktile + kKTileBytes;
       const int n = lane & 15, grp = lane >> 4;
-      // INT4: the tile's row scales (K at [0, kT), V at [kT, 2 kT))
+      // INT4: the tile's row scales (K at [0, kT), times the logit scale; V at
+      // [kT, 2 kT))
       const float* sct = reinterpret_cast<const float*>(ktile + 2 * kKTileBytes);
       // K: the 8 elements per k-block of rows 16*tg + n this lane feeds to
       // the MFMA (INT4: the lane's kKBlocks * 4 contiguous bytes, one dword
@@ -725,14 +738,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
           vraw[nb] = make_uint4(w0.x, w0.y, w1.x, w1.y);
         }
       }
-      float4 ksc[2], vsc[2];   // INT4 row scales of this lane's rows
-      if constexpr (kInt4) {
-#pragma unroll
-        for (int tg = 0; tg < 2; ++tg) {
-          ksc[tg] = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
-          vsc[tg] = *reinterpret_cast<const float4*>(sct + kT + 16 * tg + 4 * grp);
-        }
-      }
+      float4 ksc[2], vsc[2];   // INT4 row scales of this lane's rows, read where used
 
       // S^T = K q^T: lane l gets the logits of head n for rows 16*tg + 4*grp + r
       // (rows at or past row_end are masked, which only a split's last tile
@@ -754,14 +760,17 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
         }
         if constexpr (kInt4) {
-          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale
-          sacc[0] = (sacc[0] - q8[0]) * ksc[tg].x;
-          sacc[1] = (sacc[1] - q8[0]) * ksc[tg].y;
-          sacc[2] = (sacc[2] - q8[0]) * ksc[tg].z;
-          sacc[3] = (sacc[3] - q8[0]) * ksc[tg].w;
-        }
+          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale (which carries
+          // the logit scale)
+          ksc[tg] = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
+          x[tg][0] = (sacc[0] - q8[0]) * ksc[tg].x;
+          x[tg][1] = (sacc[1] - q8[0]) * ksc[tg].y;
+          x[tg][2] = (sacc[2] - q8[0]) * ksc[tg].z;
+          x[tg][3] = (sacc[3] - q8[0]) * ksc[tg].w;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[tg][r] = sacc[r] * c2;
+          for (int r = 0; r < 4; ++r) x[tg][r] = sacc[r] * c2;
+        }
       }
       if (!full) {
 #pragma unroll
@@ -810,6 +819,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       l_sum += lsum;
       if constexpr (kInt4) {
         // p times the row's V scale (rows past the sequence have scale 0 and p 0)
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg)
+          vsc[tg] = *reinterpret_cast<const float4*>(sct + kT + 16 * tg + 4 * grp);
         pv[0] *= vsc[0].x; pv[1] *= vsc[0].y; pv[2] *= vsc[0].z; pv[3] *= vsc[0].w;
         pv[4] *= vsc[1].x; pv[5] *= vsc[1].y; pv[6] *= vsc[1].z; pv[7] *= vsc[1].w;
       }
@@ -821,10 +833,11 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         // same products against a column of ones.
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
-          const uint32_t x0 = vraw[cb].x ^ 0x88888888u, x1 = vraw[cb].y ^ 0x88888888u;
-          const uint4 vlo = e4m3x8_to_bf16x8(make_uint2(x0 & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu), 512.0f);
-          const uint4 vhi = e4m3x8_to_bf16x8(
-              make_uint2((x0 >> 4) & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu), 512.0f);
+          const uint32_t x0 = vraw[cb].x, x1 = vraw[cb].y;
+          const uint4 vlo =
+              e4m3x8_to_bf16x8(make_uint2(int4_low_offset8(x0), int4_low_offset8(x1)), 512.0f);
+          const uint4 vhi =
+              e4m3x8_to_bf16x8(make_uint2(int4_high_offset8(x0), int4_high_offset8(x1)), 512.0f);
           oacc[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vlo), oacc[2 * cb], 0, 0, 0);
           oacc[2 * cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vlo), oacc[2 * cb], 0, 0, 0);
           oacc[2 * cb + 1] =
