@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="index into workloads.CONFIGS")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
+    ap.add_argument("--hq", type=int, default=0,
+                    help="query heads instead of the config's own (same kv-heads, lengths and "
+                         "seed), e.g. --config 1 --hq 128 for groups of 16 heads")
     ap.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8", "int4"), default="bf16",
                     help="K/V cache element: bf16, E4M3 codes with per-kv-head scales, or "
@@ -186,6 +189,10 @@ def main():
     das.load_library()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.config]
+    if args.hq:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_hq{args.hq}", Hq=args.hq,
+                                  description=f"{cfg.description}, Hq={args.hq} instead")
     int4 = args.kv_dtype == "int4"
     fp8 = args.kv_dtype == "fp8"
     quant = fp8 or int4      # codes plus fp32 scales
@@ -197,9 +204,9 @@ def main():
         paged = workloads.make_paged_inputs(cfg, 42 + args.config, args.paged, layout, fp8=fp8)
         x = paged.base
     elif int4:
-        x = workloads.config_int4_inputs(args.config)
+        x = workloads.make_int4_inputs(cfg, 42 + args.config)
     else:
-        x = workloads.config_fp8_inputs(args.config) if fp8 else workloads.config_inputs(args.config)
+        x = (workloads.make_fp8_inputs if fp8 else workloads.make_inputs)(cfg, 42 + args.config)
     B, Hq, D = x.q.shape
     Hkv, Smax = x.k.shape[1], x.k.shape[2]
     kv_bytes = x.kv_bytes

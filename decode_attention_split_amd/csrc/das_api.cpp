@@ -52,11 +52,15 @@ int64_t round_up(int64_t a, int64_t q) { return ceil_div(a, q) * q; }
 // of partial state per D*4 bytes of K+V row, so the partial traffic is about
 // 2*G/chunk of the K/V bytes (written once, read once); these floors keep it
 // near 3%.
-int64_t min_chunk(int G) { return G >= 8 ? 512 : 256; }
+int64_t min_chunk(int G) { return G >= 16 ? 1024 : (G >= 8 ? 512 : 256); }
 
 bool supported_dims(int D, int G) {
-  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
+  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
+
+// GQA groups of 16 heads need a wave's end-of-stream state (16 heads x D
+// floats) to fit in its tile region, which the INT4 tiles are too small for.
+bool format_supports_group(int format, int G) { return format != das::kKvInt4 || G <= 8; }
 
 int device_cus(int32_t num_cus, int* out) {
   if (num_cus > 0) {
@@ -284,6 +288,7 @@ int split_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
                               num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c);
   if (rc != DAS_OK) return rc;
+  if (!format_supports_group(kv.format, c.G)) return DAS_ENOTSUP;
   return run_phase1(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                     workspace, c, false, static_cast<hipStream_t>(stream));
 }
@@ -299,6 +304,7 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
                               num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c,
                               kv.page_size, wgs_for_format(kv.format));
   if (rc != DAS_OK) return rc;
+  if (!format_supports_group(kv.format, c.G)) return DAS_ENOTSUP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One launch: the last workgroup of each (b, kv-head) merges the splits.
   // Every split workgroup then ends with a store-completion wait and a
@@ -337,6 +343,7 @@ int das_plan_kv(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t G, int32_t Sma
     case DAS_INT4: format = das::kKvInt4; break;
     default: return DAS_EINVAL;
   }
+  if (!format_supports_group(format, G)) return DAS_ENOTSUP;
   return plan_impl(B, Hkv, G, Smax, D, num_splits, num_cus, ns_out, chunk_out,
                    wgs_for_format(format));
 }

@@ -796,11 +796,16 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         const float alpha = fast_exp2(m_lane - mn);   // 0 on the first tile
         l_sum *= alpha;
         // row r of this lane's accumulators is head 4*grp + r, whose factor
-        // the lane with n = 4*grp + r holds (G = 4: heads 0..3 in group 0)
+        // the lane with n = 4*grp + r holds (G = 4: heads 0..3 in group 0;
+        // rows of heads >= G are padding)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float f = lane_value(alpha, r);
-          if constexpr (G == 8) f = grp == 1 ? lane_value(alpha, 4 + r) : f;
+          if constexpr (G >= 8) f = grp == 1 ? lane_value(alpha, 4 + r) : f;
+          if constexpr (G >= 16) {
+            f = grp == 2 ? lane_value(alpha, 8 + r) : f;
+            f = grp == 3 ? lane_value(alpha, 12 + r) : f;
+          }
 #pragma unroll
           for (int nb = 0; nb < kNBlocks; ++nb) oacc[nb][r] *= f;
           if constexpr (kInt4) osum[r] *= f;
@@ -1202,8 +1207,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // The loads are bound by the CU's address rate, so each 16-lane row (one
   // head, one split group: kGroupLanes is 16 or 32 and divides kQuads) loads
   // the batch's (max, sum) pairs once, lane x the pair of split x % 8, and
-  // hands them round with row broadcasts.
-  static_assert(kGroupLanes % 16 == 0 && kQuads % kGroupLanes == 0, "one head per row");
+  // hands them round with row broadcasts.  (kGroupLanes and kQuads are
+  // multiples of 16, so no row spans two heads or two split groups.)
+  static_assert(kGroupLanes % 16 == 0 && kQuads % 16 == 0, "one head per row");
   float mt = -INFINITY;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float ls = 0.f;
@@ -1460,6 +1466,9 @@ static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bo
       case 2: return launch_split<128, 2, kKv, kPaged>(B, a, one_per_cu, st);
       case 4: return launch_split<128, 4, kKv, kPaged>(B, a, one_per_cu, st);
       case 8: return launch_split<128, 8, kKv, kPaged>(B, a, one_per_cu, st);
+      case 16:
+        if constexpr (kKv != kKvInt4) return launch_split<128, 16, kKv, kPaged>(B, a, one_per_cu, st);
+        break;
     }
   } else if (D == 64) {
     switch (G) {
@@ -1467,6 +1476,9 @@ static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bo
       case 2: return launch_split<64, 2, kKv, kPaged>(B, a, one_per_cu, st);
       case 4: return launch_split<64, 4, kKv, kPaged>(B, a, one_per_cu, st);
       case 8: return launch_split<64, 8, kKv, kPaged>(B, a, one_per_cu, st);
+      case 16:
+        if constexpr (kKv != kKvInt4) return launch_split<64, 16, kKv, kPaged>(B, a, one_per_cu, st);
+        break;
     }
   }
   return hipErrorInvalidValue;

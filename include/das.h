@@ -45,7 +45,8 @@
  *     stream-ordered; the call returns without waiting for the GPU.
  *   - Calls are re-entrant.  Concurrent calls must not share a workspace.
  *   - Supported shapes: head dim D in {64, 128}; GQA group G = Hq / Hkv in
- *     {1, 2, 4, 8} (Hq a multiple of Hkv); 1 <= B <= 65535; 1 <= Hkv <= 65535;
+ *     {1, 2, 4, 8, 16} (Hq a multiple of Hkv; 16 with bf16 and E4M3 caches,
+ *     DAS_ENOTSUP with INT4); 1 <= B <= 65535; 1 <= Hkv <= 65535;
  *     1 <= Smax with (Smax + 256) * D * 2 < 2^31 (one sequence's K rows are
  *     addressed with 32-bit byte offsets); num_splits <= DAS_MAX_SPLITS.
  *   - Query head h reads kv-head h / G.

@@ -14,7 +14,7 @@ from gpu_helpers import check_bf16, check_f32, dev, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8)]
+SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8, 16)]
 
 
 def upload_fp8(x: workloads.Fp8Inputs):

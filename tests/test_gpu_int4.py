@@ -142,3 +142,13 @@ def test_int4_named_config_full_size(idx):
     assert d_o <= 5e-4 and d_l <= 1e-4
     del t
     torch.cuda.empty_cache()
+
+
+def test_int4_group_of_16_is_not_supported():
+    """A wave's end-of-stream state for 16 heads does not fit in an INT4 tile
+    region: the call is refused before anything is launched."""
+    cfg = workloads.custom_config(1, 32, 2, 128, 256)
+    x = workloads.make_int4_inputs(cfg, 8500, seq_lens=(256,))
+    with pytest.raises(das.DasError) as e:
+        run_int4(x, 0)
+    assert e.value.status == das.DAS_ENOTSUP

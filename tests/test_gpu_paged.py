@@ -49,7 +49,8 @@ def ref_paged(x):
 
 
 @pytest.mark.parametrize("layout", [HND, NHD], ids=["HND", "NHD"])
-@pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128) for G in (1, 2, 4, 8)], ids=lambda v: str(v))
+@pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128) for G in (1, 2, 4, 8, 16)],
+                         ids=lambda v: str(v))
 def test_paged_small_shapes(D, G, layout):
     """Every (D, G), both pool layouts, two page sizes, several split counts."""
     cfg = workloads.custom_config(3, 2 * G, 2, D, 1000, k_mult=2.0)

@@ -10,11 +10,11 @@ import torch
 import decode_attention_split_amd as das
 import oracle
 import workloads
-from gpu_helpers import check_bf16, check_f32, note, run, upload
+from gpu_helpers import check_bf16, check_f32, note, run, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8)]
+SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8, 16)]
 
 
 @pytest.mark.parametrize("D,G", SHAPES, ids=lambda v: str(v))
@@ -30,7 +30,8 @@ def test_small_shapes_all_split_counts(D, G):
         check_f32(out, lse, *ref, f"D={D} G={G} ns={ns}")
 
 
-@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2)], ids=lambda v: str(v))
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (128, 16)],
+                         ids=lambda v: str(v))
 def test_edge_lengths(D, G):
     """Lengths around the 16/32-row tiles and the 128-row chunk quantum, with
     empty splits (forced split counts larger than a sequence needs) and L=0."""
@@ -46,7 +47,7 @@ def test_edge_lengths(D, G):
         assert torch.all(out[0] == 0) and torch.all(lse[0] == -float("inf"))
 
 
-@pytest.mark.parametrize("D,G", [(128, 4), (64, 1), (128, 8)], ids=lambda v: str(v))
+@pytest.mark.parametrize("D,G", [(128, 4), (64, 1), (128, 8), (64, 16)], ids=lambda v: str(v))
 def test_bf16_output(D, G):
     cfg = workloads.custom_config(3, 4 * G, 4, D, 2000, k_mult=4.0)
     x = workloads.make_inputs(cfg, 3000 + D + G, seq_lens=(2000, 1, 1234))
@@ -137,7 +138,7 @@ def _steer_keys(x, ramps):
     return x
 
 
-@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (64, 4)],
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (64, 4), (128, 16)],
                          ids=lambda v: str(v))
 def test_rising_falling_and_spiking_logits(D, G):
     """Logit profiles that move the running max in every way the online
@@ -162,3 +163,34 @@ def test_rising_falling_and_spiking_logits(D, G):
         note(f"case steered logits D={D} G={G} num_splits={ns}")
         out, lse = run(x, ns, tensors=t)
         check_f32(out, lse, *ref, f"steered D={D} G={G} ns={ns}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_group_of_16_at_a_405b_shape(fmt):
+    """GQA groups of 16 heads (Hq=128, Hkv=8, D=128: a Llama-3.1-405B-shaped
+    decode) over a 32K-token cache at full size, in the automatic plan, with
+    the oracle over every output; num_splits=1 must agree."""
+    cfg = workloads.custom_config(1, 128, 8, 128, 32768)
+    note(f"case G=16 405B-shaped {fmt}: generating inputs")
+    d = torch.device("cuda:0")
+    if fmt == "bf16":
+        x = workloads.make_inputs(cfg, 4300, seq_lens=(32768,))
+        ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+        t = upload(x)
+        call = lambda ns: run(x, ns, tensors=t)
+    else:
+        x = workloads.make_fp8_inputs(cfg, 4301, seq_lens=(32768,))
+        ref = oracle.attention_fp8(x.q, x.k, x.v, x.k_scale, x.v_scale, x.seq_lens, x.scale)
+        q = to_dev(x.q)
+        k, v = torch.from_numpy(x.k).to(d), torch.from_numpy(x.v).to(d)
+        ks, vs = torch.from_numpy(x.k_scale).to(d), torch.from_numpy(x.v_scale).to(d)
+        sl = torch.from_numpy(x.seq_lens).to(d)
+
+        def call(ns):
+            o, l = das.das_decode_attention_fp8(q, k, v, ks, vs, sl, x.scale, num_splits=ns)
+            torch.cuda.synchronize()
+            return o, l
+    for ns in (0, 1):
+        note(f"case G=16 405B-shaped {fmt}: num_splits={ns}")
+        out, lse = call(ns)
+        check_f32(out, lse, *ref, f"G=16 {fmt} ns={ns}")

@@ -30,10 +30,12 @@ FORMATS = ("bf16", "fp8", "int4", "paged", "paged_fp8")
 def draw_case(seed: int) -> dict:
     rng = np.random.Generator(np.random.PCG64(seed))
     D = int(rng.choice([64, 128]))
-    G = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
     Hkv = int(rng.integers(1, 5))
     B = int(rng.integers(1, 9))
     fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
+    if fmt == "int4" and G == 16:
+        G = 8     # INT4 caches support groups of up to 8 heads
     smax = int(np.exp(rng.uniform(0.0, np.log(20000.0))))   # log-uniform, 1 .. 20000
     page = int(rng.choice([32, 64, 128, 256])) if fmt.startswith("paged") else 0
     # lengths: uniform, plus edge values around 32-row tiles and pages

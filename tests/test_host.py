@@ -273,3 +273,17 @@ def _call_paged(lib, **kw):
 def test_paged_argument_checks(lib, kw, status):
     # All pointers are fake: a failed check must return before any launch.
     assert _call_paged(lib, **kw) == status
+
+
+def test_group_of_16_plans_and_int4_refuses_it():
+    # G = 16 (e.g. Hq = 128, Hkv = 8): bf16 and E4M3 caches plan as usual with
+    # chunks of at least 1024 rows; an INT4 cache does not support it
+    ns, chunk = plan(1, 8, 16, 32768, 128)
+    assert chunk >= 1024 and (ns - 1) * chunk < 32768 <= ns * chunk
+    assert das.das_plan_kv(das.DAS_E4M3, 1, 8, 16, 32768, 128, 0, 256) == (ns, chunk)
+    with pytest.raises(das.DasError) as e:
+        das.das_plan_kv(das.DAS_INT4, 1, 8, 16, 32768, 128, 0, 256)
+    assert e.value.status == das.DAS_ENOTSUP
+    with pytest.raises(das.DasError) as e:
+        das.das_plan(1, 8, 32, 32768, 128, 0, 256)          # G = 32
+    assert e.value.status == das.DAS_ENOTSUP
