@@ -70,6 +70,10 @@ def parse():
                          "never as, the value)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time for the oracle baseline; 0 skips it")
+    ap.add_argument("--op", choices=("decode", "merge"), default="decode",
+                    help="decode: the decode-attention call (the headline); merge: "
+                         "das_merge_attn_states alone, at one decode step's rows and at a "
+                         "bandwidth-sized call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -90,6 +94,66 @@ def calibrate_copy() -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                       "launches": 10}), flush=True)
+
+
+def bench_merge(args) -> None:
+    """das_merge_attn_states ([SGL-PAR] "Constraints": the LSE merge of two
+    partial states, as a sequence-parallel decode ends with) on fp32 states
+    of D = 128: HBM bytes per call 3 * rows * (D + 1) * 4 (two states read,
+    one written).  Times args.steps calls back to back after args.warmup,
+    with HIP events on the launch stream, at rows = 2048 (one decode step of
+    B=64 x Hq=32) and rows = 2^20."""
+    import ctypes
+
+    import torch
+
+    import decode_attention_split_amd as das
+
+    lib = das.load_library()
+    dev = torch.device("cuda:0")
+    D = 128
+    sizes = []
+    for rows in (2048, 1 << 20):
+        g = torch.Generator().manual_seed(rows)
+        o_a = torch.randn(rows, D, generator=g).to(dev)
+        o_b = torch.randn(rows, D, generator=g).to(dev)
+        lse_a = (4 * torch.randn(rows, generator=g)).to(dev)
+        lse_b = (4 * torch.randn(rows, generator=g)).to(dev)
+        o_out, lse_out = torch.empty_like(o_a), torch.empty_like(lse_a)
+        ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (o_a, lse_a, o_b, lse_b, o_out, lse_out)]
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def call():
+            rc = lib.das_merge_attn_states(*ptrs, rows, D, das.DAS_F32, stream)
+            if rc != 0:
+                raise RuntimeError(f"das_merge_attn_states: status {rc}")
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        nbytes = 3 * rows * (D + 1) * 4
+        sizes.append({"rows": rows, "D": D, "bytes_per_call": nbytes, "us_per_call": round(us, 3),
+                      "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)})
+    big = sizes[-1]
+    print(json.dumps({
+        "metric": "merge_attn_states HBM GB/s (% of peak) and us per call",
+        "value": big["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(big["us_per_call"] / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "merge_attn_states_f32_d128", "sizes": sizes},
+        "roofline": {"bound": "hbm", "kernel": "merge_attn_states", "achieved": big["GB/s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(big["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
 
 
 def kernel_source_digest() -> str:
@@ -179,6 +243,9 @@ def main():
                          "(each GPU would run the same kernel on its own share of the "
                          "sequences); run with --gpus 1.\n")
         sys.exit(2)
+    if args.op == "merge":
+        bench_merge(args)
+        return
 
     import numpy as np
     import torch

@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "das_internal.h"
@@ -1373,57 +1374,88 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
 }
 
 // ---------------------------------------------------------------------------
-// merge_attn_states: one wave per row, so that every lane has read the row's
-// two LSE values before lane 0 may overwrite one of them in place.
+// merge_attn_states ([SGL-PAR] "Constraints": the LSE merge of two partial
+// attention states).  Each lane handles four consecutive elements of a row
+// (16-byte f32 or 8-byte bf16 accesses), D/4 lanes per row, so a row lies
+// within one wave: every lane of the row has read its two LSE values before
+// one lane may overwrite one of them in place, and every element is read
+// and written by the same lane.  A grid-stride loop over groups of rows.
 // ---------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+#ifndef DAS_MERGE_UNROLL
+#define DAS_MERGE_UNROLL 4
+#endif
+constexpr int kMergeUnroll = DAS_MERGE_UNROLL;
+
+template <int D>
+constexpr int merge_rows_per_block() { return kMergeThreads / (D / 4); }
+
 template <int D, bool kBf16>
-__global__ __launch_bounds__(256) void merge_attn_states_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_attn_states_kernel(MergeArgs a) {
   // No contraction into FMAs: wa*oa and wb*ob must round the same way so that
   // swapping the two states gives bitwise the same result.
 #pragma clang fp contract(off)
-  constexpr int kPer = D / 64;  // elements per lane
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= a.rows) return;
-  const float la = a.lse_a[row], lb = a.lse_b[row];
-  const float mx = fmaxf(la, lb);
-  float wa = 0.f, wb = 0.f, lse = -INFINITY;
-  if (mx != -INFINITY) {
-    lse = mx + logf(expf(la - mx) + expf(lb - mx));
-    wa = expf(la - lse);
-    wb = expf(lb - lse);
-  }
-  float oa[kPer], ob[kPer];
-  const size_t base = (size_t)row * D + (size_t)lane * kPer;
-  if constexpr (kBf16) {
-    const uint16_t* pa = reinterpret_cast<const uint16_t*>(a.o_a) + base;
-    const uint16_t* pb = reinterpret_cast<const uint16_t*>(a.o_b) + base;
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRows = merge_rows_per_block<D>();
+  // Rows per lane per pass: all their loads are issued before any store (a
+  // store may alias a later row's input, so the compiler cannot hoist loads
+  // past it), which keeps kUnroll rows of each lane in flight.
+  constexpr int kUnroll = kMergeUnroll;
+  const int sub = threadIdx.x / kLanesPerRow;        // row within a group of kRows
+  const int c = (threadIdx.x % kLanesPerRow) * 4;    // first element of this lane
+  const int64_t step = (int64_t)gridDim.x * kRows * kUnroll;
+  for (int64_t row0 = (int64_t)blockIdx.x * kRows * kUnroll + sub; row0 < a.rows; row0 += step) {
+    float la[kUnroll], lb[kUnroll], oa[kUnroll][4], ob[kUnroll][4];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      oa[i] = __uint_as_float((uint32_t)pa[i] << 16);
-      ob[i] = __uint_as_float((uint32_t)pb[i] << 16);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = row0 + (int64_t)u * kRows;
+      if (row >= a.rows) break;
+      la[u] = a.lse_a[row];
+      lb[u] = a.lse_b[row];
+      const size_t base = (size_t)row * D + c;
+      if constexpr (kBf16) {
+        const uint2 ua = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.o_a) + base);
+        const uint2 ub = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.o_b) + base);
+        oa[u][0] = bf16_lo(ua.x); oa[u][1] = bf16_hi(ua.x); oa[u][2] = bf16_lo(ua.y); oa[u][3] = bf16_hi(ua.y);
+        ob[u][0] = bf16_lo(ub.x); ob[u][1] = bf16_hi(ub.x); ob[u][2] = bf16_lo(ub.y); ob[u][3] = bf16_hi(ub.y);
+      } else {
+        const float4 fa = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.o_a) + base);
+        const float4 fb = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.o_b) + base);
+        oa[u][0] = fa.x; oa[u][1] = fa.y; oa[u][2] = fa.z; oa[u][3] = fa.w;
+        ob[u][0] = fb.x; ob[u][1] = fb.y; ob[u][2] = fb.z; ob[u][3] = fb.w;
+      }
     }
-  } else {
-    const float* pa = reinterpret_cast<const float*>(a.o_a) + base;
-    const float* pb = reinterpret_cast<const float*>(a.o_b) + base;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      oa[i] = pa[i];
-      ob[i] = pb[i];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = row0 + (int64_t)u * kRows;
+      if (row >= a.rows) break;
+      const float mx = fmaxf(la[u], lb[u]);
+      float wa = 0.f, wb = 0.f, lse = -INFINITY;
+      if (mx != -INFINITY) {
+        lse = mx + logf(expf(la[u] - mx) + expf(lb[u] - mx));
+        wa = expf(la[u] - lse);
+        wb = expf(lb[u] - lse);
+      }
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // products rounded separately so that swapping a and b is bitwise symmetric
+        const float ta = wa * oa[u][i];
+        const float tb = wb * ob[u][i];
+        v[i] = (mx == -INFINITY) ? 0.f : ta + tb;
+      }
+      const size_t base = (size_t)row * D + c;
+      if constexpr (kBf16) {
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o_out) + base) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o_out) + base) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (c == 0) a.lse_out[row] = lse;
     }
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    // products rounded separately so that swapping a and b is bitwise symmetric
-    const float ta = wa * oa[i];
-    const float tb = wb * ob[i];
-    const float v = (mx == -INFINITY) ? 0.f : ta + tb;
-    if constexpr (kBf16)
-      reinterpret_cast<uint16_t*>(a.o_out)[base + i] = f32_to_bf16_rne(v);
-    else
-      reinterpret_cast<float*>(a.o_out)[base + i] = v;
-  }
-  if (lane == 0) a.lse_out[row] = lse;
 }
 
 }  // namespace
@@ -1513,17 +1545,24 @@ hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st
 
 hipError_t launch_merge_attn_states(int D, const MergeArgs& a, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
-  dim3 grid((unsigned)((a.rows + 3) / 4));
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
+  // One pass per block up to 65536 blocks (2M rows of D = 128): a block per
+  // group of rows measured faster than fewer blocks looping (1M rows: 285 us
+  // against 302 us with 2048 blocks); larger calls loop.
+  constexpr int64_t kMaxBlocks = 65536;
+  const int64_t rows_per_block =
+      (D == 128 ? merge_rows_per_block<128>() : merge_rows_per_block<64>()) * kMergeUnroll;
+  const dim3 grid((unsigned)std::min<int64_t>((a.rows + rows_per_block - 1) / rows_per_block,
+                                              kMaxBlocks));
+  const dim3 block(kMergeThreads);
   if (D == 128 && a.bf16)
-    hipLaunchKernelGGL((merge_attn_states_kernel<128, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((merge_attn_states_kernel<128, true>), grid, block, 0, st, a);
   else if (D == 128)
-    hipLaunchKernelGGL((merge_attn_states_kernel<128, false>), grid, dim3(256), 0, st, a);
-  else if (D == 64 && a.bf16)
-    hipLaunchKernelGGL((merge_attn_states_kernel<64, true>), grid, dim3(256), 0, st, a);
-  else if (D == 64)
-    hipLaunchKernelGGL((merge_attn_states_kernel<64, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((merge_attn_states_kernel<128, false>), grid, block, 0, st, a);
+  else if (a.bf16)
+    hipLaunchKernelGGL((merge_attn_states_kernel<64, true>), grid, block, 0, st, a);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((merge_attn_states_kernel<64, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
