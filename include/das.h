@@ -95,10 +95,13 @@ typedef enum {
 /*
  * Split plan ([FD++] §2 grid, §6 tuning guide).  Pure host function.
  *   num_splits == 0: automatic.  The plan picks the number of splits NS so
- *     that B*Hkv*NS workgroups give every compute unit several workgroups,
- *     with chunk = ceil(Smax/NS) rounded up to DAS_CHUNK_QUANTUM and kept
- *     between a lower bound (partial-result traffic stays a few percent of
- *     the K/V bytes) and an upper bound.
+ *     that the B*Hkv*NS workgroups about fill the chip -- three for every four
+ *     compute units, which already saturate HBM (das_plan_kv: every compute
+ *     unit for an INT4 cache) -- while the longest sequence is cut into at
+ *     least five splits, with chunk = ceil(Smax/NS) rounded up to
+ *     DAS_CHUNK_QUANTUM and kept between a lower bound (partial-result
+ *     traffic stays a few percent of the K/V bytes: 256 rows, 512 for G = 8,
+ *     1024 for G = 16) and an upper bound (8192 rows).
  *   num_splits == n >= 1: chunk = ceil(Smax/n) rounded up to the quantum;
  *     NS = ceil(Smax/chunk) <= n.
  *   Sequence b uses ceil(seq_lens[b]/chunk) of the NS splits; the rest exit
