@@ -97,8 +97,8 @@ typedef enum {
  *   num_splits == 0: automatic.  The plan picks the number of splits NS so
  *     that the B*Hkv*NS workgroups about fill the chip -- three for every four
  *     compute units, which already saturate HBM (das_plan_kv: every compute
- *     unit for an INT4 cache) -- while the longest sequence is cut into at
- *     least five splits, with chunk = ceil(Smax/NS) rounded up to
+ *     unit for an INT4 cache) -- and the longest sequence into at least five
+ *     splits where the chunk bounds allow, with chunk = ceil(Smax/NS) rounded up to
  *     DAS_CHUNK_QUANTUM and kept between a lower bound (partial-result
  *     traffic stays a few percent of the K/V bytes: 256 rows, 512 for G = 8,
  *     1024 for G = 16) and an upper bound (8192 rows).
