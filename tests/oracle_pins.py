@@ -171,7 +171,7 @@ def pin_identical_keys_give_mean(lib):
 
 def pin_gqa_head_mapping(lib):
     """kv-head g holds constant V = 2^g: query head h must return 2^(h // G) exactly."""
-    for Hq, Hkv in ((8, 2), (8, 8), (8, 1), (6, 3)):
+    for Hq, Hkv in ((8, 2), (8, 8), (8, 1), (6, 3), (32, 2)):
         x = _small(16, B=2, Hq=Hq, Hkv=Hkv, D=4, smax=10, lens=(10, 6))
         v = np.zeros_like(x.v)
         for g in range(Hkv):
