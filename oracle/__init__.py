@@ -33,6 +33,12 @@ Pieces:
 * ``merge`` -- the LSE / online-softmax merge of two attention states that
   the SGLang Diffusion "Parallelism Overview" page relies on for ring hops and
   tail parts ("What happens to the shapes", "Constraints").
+* ``abs_attention`` / ``abs_attention_fp8`` / ``abs_attention_int4`` /
+  ``abs_attention_paged`` -- the same definitions with every V element
+  replaced by its absolute value, out = sum_j w_j |v_j| / Z: the magnitude of
+  the terms an output averages.  Rounding inside a kernel moves an output by
+  an amount relative to this magnitude, not to the output itself, which can
+  cancel to near zero; the bf16-output tolerance is stated in terms of it.
 * ``round_to_bf16`` -- fp64 to bfloat16, round-to-nearest-even, directly from
   fp64 (no fp32 step), for the bf16-output tolerance.
 * ``attention_fsum_textbook`` -- pure-Python brute force with ``math.fsum``
@@ -96,9 +102,10 @@ class OracleLib:
         lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i32 = ctypes.c_int32
-        lib.das_oracle_attention.argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
-                                             ctypes.c_double, p, p]
-        lib.das_oracle_attention.restype = None
+        for name in ("das_oracle_attention", "das_oracle_abs_attention"):
+            getattr(lib, name).argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
+                                           ctypes.c_double, p, p]
+            getattr(lib, name).restype = None
         lib.das_oracle_split_attention.argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
                                                    ctypes.c_double, i32, p, p]
         lib.das_oracle_split_attention.restype = None
@@ -106,14 +113,13 @@ class OracleLib:
         lib.das_oracle_merge.restype = None
         lib.das_oracle_e4m3_decode.argtypes = [p, ctypes.c_int64, p]
         lib.das_oracle_e4m3_decode.restype = None
-        lib.das_oracle_attention_fp8.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
-                                                 ctypes.c_double, p, p]
-        lib.das_oracle_attention_fp8.restype = None
+        for name in ("das_oracle_attention_fp8", "das_oracle_abs_attention_fp8",
+                     "das_oracle_attention_int4", "das_oracle_abs_attention_int4"):
+            getattr(lib, name).argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                           ctypes.c_double, p, p]
+            getattr(lib, name).restype = None
         lib.das_oracle_int4_decode.argtypes = [p, ctypes.c_int64, p]
         lib.das_oracle_int4_decode.restype = None
-        lib.das_oracle_attention_int4.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32,
-                                                  ctypes.c_double, p, p]
-        lib.das_oracle_attention_int4.restype = None
         lib.das_oracle_max_threads.argtypes = []
         lib.das_oracle_max_threads.restype = ctypes.c_int
         lib.das_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -127,16 +133,22 @@ class OracleLib:
     def set_threads(self, n: int) -> None:
         self.lib.das_oracle_set_threads(int(n))
 
-    def attention(self, q, k, v, seq_lens, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    def attention(self, q, k, v, seq_lens, scale: float,
+                  _fn: str = "das_oracle_attention") -> Tuple[np.ndarray, np.ndarray]:
         """Unsplit fp64 attention.  Inputs are bf16 bit arrays (uint16)."""
         q, k, v, seq_lens = _check_inputs(q, k, v, seq_lens)
         B, Hq, D = q.shape
         Hkv, smax = k.shape[1], k.shape[2]
         out = np.empty((B, Hq, D), dtype=np.float64)
         lse = np.empty((B, Hq), dtype=np.float64)
-        self.lib.das_oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), B, Hq, Hkv,
-                                      smax, D, float(scale), _ptr(out), _ptr(lse))
+        getattr(self.lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), B, Hq, Hkv,
+                               smax, D, float(scale), _ptr(out), _ptr(lse))
         return out, lse
+
+    def abs_attention(self, q, k, v, seq_lens, scale: float) -> np.ndarray:
+        """sum_j w_j |v_j| / Z per output element (fp64), the softmax weights
+        w_j / Z of ``attention``; 0 for an empty row set."""
+        return self.attention(q, k, v, seq_lens, scale, _fn="das_oracle_abs_attention")[0]
 
     def split_attention(self, q, k, v, seq_lens, scale: float,
                         chunk: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -160,8 +172,8 @@ class OracleLib:
         self.lib.das_oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out))
         return out
 
-    def attention_fp8(self, q, k, v, k_scale, v_scale, seq_lens,
-                      scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    def attention_fp8(self, q, k, v, k_scale, v_scale, seq_lens, scale: float,
+                      _fn: str = "das_oracle_attention_fp8") -> Tuple[np.ndarray, np.ndarray]:
         """Unsplit fp64 attention over an E4M3 K/V cache: q bf16 bits (uint16),
         k/v E4M3 codes (uint8), k_scale/v_scale fp32 per kv-head."""
         q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -180,10 +192,16 @@ class OracleLib:
             raise ValueError("k_scale and v_scale must be [Hkv]")
         out = np.empty((B, Hq, D), dtype=np.float64)
         lse = np.empty((B, Hq), dtype=np.float64)
-        self.lib.das_oracle_attention_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
-                                          _ptr(seq_lens), B, Hq, Hkv, smax, D, float(scale),
-                                          _ptr(out), _ptr(lse))
+        getattr(self.lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                               _ptr(seq_lens), B, Hq, Hkv, smax, D, float(scale),
+                               _ptr(out), _ptr(lse))
         return out, lse
+
+    def abs_attention_fp8(self, q, k, v, k_scale, v_scale, seq_lens, scale: float) -> np.ndarray:
+        """sum_j w_j |v_j| / Z over an E4M3 cache (the magnitude form of
+        ``attention_fp8``)."""
+        return self.attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale,
+                                  _fn="das_oracle_abs_attention_fp8")[0]
 
     def int4_decode(self, packed) -> np.ndarray:
         """Values of packed two's-complement INT4 codes (uint8 [..., n/2] ->
@@ -193,8 +211,8 @@ class OracleLib:
         self.lib.das_oracle_int4_decode(_ptr(packed), out.size, _ptr(out))
         return out
 
-    def attention_int4(self, q, k, v, k_scale, v_scale, seq_lens,
-                       scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    def attention_int4(self, q, k, v, k_scale, v_scale, seq_lens, scale: float,
+                       _fn: str = "das_oracle_attention_int4") -> Tuple[np.ndarray, np.ndarray]:
         """Unsplit fp64 attention over an INT4 K/V cache: q bf16 bits (uint16),
         k/v packed INT4 codes (uint8 [B,Hkv,Smax,D/2]), k_scale/v_scale fp32 per
         cached row [B,Hkv,Smax]."""
@@ -214,10 +232,16 @@ class OracleLib:
             raise ValueError("k_scale and v_scale must be [B,Hkv,Smax]")
         out = np.empty((B, Hq, D), dtype=np.float64)
         lse = np.empty((B, Hq), dtype=np.float64)
-        self.lib.das_oracle_attention_int4(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale),
-                                           _ptr(v_scale), _ptr(seq_lens), B, Hq, Hkv, smax, D,
-                                           float(scale), _ptr(out), _ptr(lse))
+        getattr(self.lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                               _ptr(seq_lens), B, Hq, Hkv, smax, D, float(scale), _ptr(out),
+                               _ptr(lse))
         return out, lse
+
+    def abs_attention_int4(self, q, k, v, k_scale, v_scale, seq_lens, scale: float) -> np.ndarray:
+        """sum_j w_j |v_j| / Z over an INT4 cache (the magnitude form of
+        ``attention_int4``)."""
+        return self.attention_int4(q, k, v, k_scale, v_scale, seq_lens, scale,
+                                   _fn="das_oracle_abs_attention_int4")[0]
 
     def merge(self, o_a, lse_a, o_b, lse_b) -> Tuple[np.ndarray, np.ndarray]:
         """LSE merge of two states; o_* are [..., D], lse_* are [...]."""
@@ -297,6 +321,27 @@ def attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, la
     k = gather_paged(k_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
     v = gather_paged(v_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
     return (lib or default()).attention(q, k, v, seq_lens, scale)
+
+
+def abs_attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, layout: int,
+                        scale: float, lib=None):
+    """sum_j w_j |v_j| / Z over a paged bf16 cache (the gathered rows)."""
+    smax = int(np.asarray(block_table).shape[1]) * page_size
+    k = gather_paged(k_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
+    v = gather_paged(v_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
+    return (lib or default()).abs_attention(q, k, v, seq_lens, scale)
+
+
+def abs_attention(q, k, v, seq_lens, scale: float):
+    return default().abs_attention(q, k, v, seq_lens, scale)
+
+
+def abs_attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale: float):
+    return default().abs_attention_fp8(q, k, v, k_scale, v_scale, seq_lens, scale)
+
+
+def abs_attention_int4(q, k, v, k_scale, v_scale, seq_lens, scale: float):
+    return default().abs_attention_int4(q, k, v, k_scale, v_scale, seq_lens, scale)
 
 
 def e4m3_decode(codes):

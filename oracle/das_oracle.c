@@ -79,16 +79,26 @@ static double logit(const uint16_t* qrow, const uint16_t* krow, int D, double sc
 }
 
 /*
+ * The value of a V element in the weighted sum: the element itself, or, for
+ * the magnitude form (absv != 0), its absolute value.
+ */
+static double vterm(double x, int absv) { return absv ? fabs(x) : x; }
+
+/*
  * Unsplit attention, the plain definition ([FD++] §1 decode step, §5 ground
  * truth):  s_j = scale * q.k_j,  M = max_j s_j,  w_j = exp(s_j - M),
  * Z = sum_j w_j,  out = sum_j w_j v_j / Z,  lse = M + ln Z.
+ * With absv != 0, out = sum_j w_j |v_j| / Z instead (elementwise absolute
+ * values): the magnitude of the terms the output averages, which bounds how
+ * far rounding can move an output that cancels to near zero.
  *
  * q: [B][Hq][D] bf16 bits; k, v: [B][Hkv][Smax][D] bf16 bits;
  * out: [B][Hq][D] double; lse: [B][Hq] double.
  */
-void das_oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                          const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                          int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+static void attention_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t Smax, int32_t D, double scale, double* out, double* lse,
+                           int absv) {
   const int G = Hq / Hkv;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
@@ -117,13 +127,26 @@ void das_oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* 
       }
       for (int j = 0; j < L; ++j) {
         const uint16_t* vrow = vbase + (size_t)j * D;
-        for (int d = 0; d < D; ++d) o[d] += w[j] * widen_bf16(vrow[d]);
+        for (int d = 0; d < D; ++d) o[d] += w[j] * vterm(widen_bf16(vrow[d]), absv);
       }
       for (int d = 0; d < D; ++d) o[d] /= Z;
       lse[(size_t)b * Hq + h] = M + log(Z);
       free(w);
     }
   }
+}
+
+void das_oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                          int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  attention_bf16(q, k, v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 0);
+}
+
+/* out = sum_j w_j |v_j| / Z: the magnitude form of das_oracle_attention. */
+void das_oracle_abs_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  attention_bf16(q, k, v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 1);
 }
 
 /*
@@ -265,10 +288,10 @@ void das_oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
  * product is exact in double: 4 + 24 significant bits).
  * k, v: [B][Hkv][Smax][D] codes; k_scale, v_scale: [Hkv] fp32.
  */
-void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
-                              const float* k_scale, const float* v_scale,
-                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                              int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+static void attention_e4m3(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                           const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                           double scale, double* out, double* lse, int absv) {
   const int G = Hq / Hkv;
   double e4m3[256];  /* the value of every code, from e4m3_value */
   for (int c = 0; c < 256; ++c) e4m3[c] = e4m3_value((uint8_t)c);
@@ -303,13 +326,29 @@ void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t
       }
       for (int j = 0; j < L; ++j) {
         const uint8_t* vrow = vbase + (size_t)j * D;
-        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * e4m3[vrow[d]]);
+        for (int d = 0; d < D; ++d) o[d] += w[j] * vterm(vs * e4m3[vrow[d]], absv);
       }
       for (int d = 0; d < D; ++d) o[d] /= Z;
       lse[(size_t)b * Hq + h] = M + log(Z);
       free(w);
     }
   }
+}
+
+void das_oracle_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  attention_e4m3(q, k, v, k_scale, v_scale, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 0);
+}
+
+/* out = sum_j w_j |v_j| / Z over the E4M3 cache: the magnitude form. */
+void das_oracle_abs_attention_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t Smax, int32_t D, double scale, double* out,
+                                  double* lse) {
+  attention_e4m3(q, k, v, k_scale, v_scale, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 1);
 }
 
 /*
@@ -337,10 +376,10 @@ void das_oracle_int4_decode(const uint8_t* packed, int64_t n, double* out) {
  * (exact in double).  k, v: [B][Hkv][Smax][D/2] bytes; k_scale, v_scale:
  * [B][Hkv][Smax] fp32.
  */
-void das_oracle_attention_int4(const uint16_t* q, const uint8_t* k, const uint8_t* v,
-                               const float* k_scale, const float* v_scale,
-                               const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                               int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+static void attention_i4(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                         const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                         int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax, int32_t D,
+                         double scale, double* out, double* lse, int absv) {
   const int G = Hq / Hkv;
   const int row_bytes = D / 2;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -375,11 +414,28 @@ void das_oracle_attention_int4(const uint16_t* q, const uint8_t* k, const uint8_
       for (int j = 0; j < L; ++j) {
         const uint8_t* vrow = v + (slab + j) * row_bytes;
         const double vs = (double)v_scale[slab + j];
-        for (int d = 0; d < D; ++d) o[d] += w[j] * (vs * (double)int4_value(vrow[d / 2], d & 1));
+        for (int d = 0; d < D; ++d)
+          o[d] += w[j] * vterm(vs * (double)int4_value(vrow[d / 2], d & 1), absv);
       }
       for (int d = 0; d < D; ++d) o[d] /= Z;
       lse[(size_t)b * Hq + h] = M + log(Z);
       free(w);
     }
   }
+}
+
+void das_oracle_attention_int4(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                               int32_t Smax, int32_t D, double scale, double* out, double* lse) {
+  attention_i4(q, k, v, k_scale, v_scale, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 0);
+}
+
+/* out = sum_j w_j |v_j| / Z over the INT4 cache: the magnitude form. */
+void das_oracle_abs_attention_int4(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t Smax, int32_t D, double scale, double* out,
+                                   double* lse) {
+  attention_i4(q, k, v, k_scale, v_scale, seq_lens, B, Hq, Hkv, Smax, D, scale, out, lse, 1);
 }

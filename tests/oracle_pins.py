@@ -540,6 +540,94 @@ def pin_paged_attention_equals_contiguous(lib):
     assert np.array_equal(o, ro) and np.array_equal(l, rl)
 
 
+# ---- magnitude form: sum_j w_j |v_j| / Z (the scale of the bf16-output bound) ----
+
+def pin_abs_zero_query_gives_mean_magnitude(lib):
+    """q = 0: every weight is 1/L, so the magnitude form is the exact mean of
+    |v| over the valid rows, for bf16, E4M3 and INT4 caches (with V scales of
+    both signs for the last two)."""
+    x = _small(51, lens=(24, 13))
+    q0 = np.zeros_like(x.q)
+    m = lib.abs_attention(q0, x.k, x.v, x.seq_lens, x.scale)
+    # negative V scales on some heads / rows: the magnitude is |scale * value|
+    xf = _small_fp8(52)
+    xf.v_scale[1::2] *= -1
+    mf = lib.abs_attention_fp8(np.zeros_like(xf.q), xf.k, xf.v, xf.k_scale, xf.v_scale,
+                               xf.seq_lens, xf.scale)
+    xi = _small_int4(53)
+    xi.v_scale[:, :, ::2] *= -1
+    mi = lib.abs_attention_int4(np.zeros_like(xi.q), xi.k, xi.v, xi.k_scale, xi.v_scale,
+                                xi.seq_lens, xi.scale)
+    import torch
+    dec8 = torch.from_numpy(np.ascontiguousarray(xf.v)).view(torch.float8_e4m3fn).double().numpy()
+    dec4 = _int4_by_shifts(xi.v)
+    G = x.q.shape[1] // x.k.shape[1]
+    for b in range(2):
+        for h in range(x.q.shape[1]):
+            g = h // G
+            L = int(x.seq_lens[b])
+            rows = np.abs(_f(x.v[b, g, :L]))
+            _close(m[b, h], [math.fsum(rows[:, d]) / L for d in range(rows.shape[1])], 1e-14,
+                   "bf16 q=0 mean |v|")
+            L = int(xf.seq_lens[b])
+            rows = np.abs(float(xf.v_scale[g]) * dec8[b, g, :L])
+            _close(mf[b, h], [math.fsum(rows[:, d]) / L for d in range(rows.shape[1])], 1e-14,
+                   "E4M3 q=0 mean |v|")
+            L = int(xi.seq_lens[b])
+            rows = np.abs(xi.v_scale[b, g, :L, None].astype(np.float64) * dec4[b, g, :L])
+            _close(mi[b, h], [math.fsum(rows[:, d]) / L for d in range(rows.shape[1])], 1e-14,
+                   "INT4 q=0 mean |v|")
+
+
+def pin_abs_one_signed_values_equal_the_output(lib):
+    """When every V element has one sign the magnitude form is |out|: bitwise
+    out itself for non-negative V and -out for non-positive V (bf16 sign bits
+    cleared or set; E4M3 sign bits cleared; INT4 nibbles limited to 0..7)."""
+    x = _small(54, lens=(24, 9))
+    pos = x.v & np.uint16(0x7FFF)
+    neg = x.v | np.uint16(0x8000)
+    o, _ = lib.attention(x.q, x.k, pos, x.seq_lens, x.scale)
+    assert np.array_equal(lib.abs_attention(x.q, x.k, pos, x.seq_lens, x.scale), o)
+    o, _ = lib.attention(x.q, x.k, neg, x.seq_lens, x.scale)
+    assert np.array_equal(lib.abs_attention(x.q, x.k, neg, x.seq_lens, x.scale), -o)
+    xf = _small_fp8(55)
+    vf = xf.v & np.uint8(0x7F)
+    o, _ = lib.attention_fp8(xf.q, xf.k, vf, xf.k_scale, xf.v_scale, xf.seq_lens, xf.scale)
+    assert np.array_equal(lib.abs_attention_fp8(xf.q, xf.k, vf, xf.k_scale, xf.v_scale,
+                                                xf.seq_lens, xf.scale), o)
+    xi = _small_int4(56)
+    vi = xi.v & np.uint8(0x77)
+    o, _ = lib.attention_int4(xi.q, xi.k, vi, xi.k_scale, xi.v_scale, xi.seq_lens, xi.scale)
+    assert np.array_equal(lib.abs_attention_int4(xi.q, xi.k, vi, xi.k_scale, xi.v_scale,
+                                                 xi.seq_lens, xi.scale), o)
+
+
+def pin_abs_bruteforce_tiny(lib):
+    """The magnitude form against a pure-Python textbook sum with math.fsum:
+    sum_j exp(s_j) |v_j| / sum_j exp(s_j)."""
+    x = _small(57, B=2, Hq=4, Hkv=2, D=8, smax=20, lens=(20, 5))
+    m = lib.abs_attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    for b, L in enumerate(x.seq_lens):
+        for h in range(4):
+            g = h // 2
+            qv, ks, vs = _f(x.q[b, h]), _f(x.k[b, g, :L]), _f(x.v[b, g, :L])
+            e = [math.exp(x.scale * math.fsum(qv * ks[j])) for j in range(L)]
+            Z = math.fsum(e)
+            want = [math.fsum(e[j] * abs(vs[j, d]) for j in range(L)) / Z for d in range(8)]
+            _close(m[b, h], want, 1e-13, f"magnitude brute force b={b} h={h}")
+
+
+def pin_abs_bounds_the_output(lib):
+    """Triangle inequality: |out| <= magnitude everywhere, strictly somewhere
+    for random V of both signs; an empty sequence gives 0."""
+    x = _small(58, lens=(24, 0))
+    o, _ = lib.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    m = lib.abs_attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    assert np.all(np.abs(o) <= m * (1 + 1e-15)), "|out| must not exceed the magnitude"
+    assert np.any(np.abs(o[0]) < 0.5 * m[0]), "random signs must cancel somewhere"
+    assert np.all(m[1] == 0.0), "an empty sequence has magnitude 0"
+
+
 ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_") and callable(v)),
                   key=lambda f: (f is pin_fd_equivalence_check, f.__name__))
 

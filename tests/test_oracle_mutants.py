@@ -29,8 +29,8 @@ MUTANTS = [
      "dot += widen_bf16(qrow[d]) * widen_bf16(krow[D - 1 - d]);"),
     ("value_rows_reversed", "const uint16_t* vrow = vbase + (size_t)j * D;\n        for (int d = 0; d < D; ++d) o[d] += w[j]",
      "const uint16_t* vrow = vbase + (size_t)(L - 1 - j) * D;\n        for (int d = 0; d < D; ++d) o[d] += w[j]"),
-    ("value_weight_dropped", "for (int d = 0; d < D; ++d) o[d] += w[j] * widen_bf16(vrow[d]);",
-     "for (int d = 0; d < D; ++d) o[d] += widen_bf16(vrow[d]);"),
+    ("value_weight_dropped", "o[d] += w[j] * vterm(widen_bf16(vrow[d]), absv);",
+     "o[d] += vterm(widen_bf16(vrow[d]), absv);"),
     ("merge_lse_drops_max", "const double lse = mx + log(exp(a - mx) + exp(b - mx));",
      "const double lse = log(exp(a - mx) + exp(b - mx));"),
     ("merge_weights_swapped", "const double wa = exp(a - lse), wb = exp(b - lse);",
@@ -42,7 +42,7 @@ MUTANTS = [
     ("e4m3_no_nan", "if (e == 15 && m == 7) return NAN;", ""),
     ("e4m3_mantissa_over_16", "v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 16.0, e - 7);"),
     ("fp8_k_scale_dropped", "(ks * e4m3[krow[d]])", "e4m3[krow[d]]"),
-    ("fp8_v_scale_from_k", "(vs * e4m3[vrow[d]])", "(ks * e4m3[vrow[d]])"),
+    ("fp8_v_scale_from_k", "vterm(vs * e4m3[vrow[d]], absv)", "vterm(ks * e4m3[vrow[d]], absv)"),
     ("fp8_scale_first_head", "const double ks = (double)k_scale[g]", "const double ks = (double)k_scale[0]"),
     ("int4_unsigned", "return n >= 8 ? n - 16 : n;", "return n;"),
     ("int4_high_nibble_first", "const int n = high ? (byte >> 4) : (byte & 15);",
@@ -56,6 +56,11 @@ MUTANTS = [
      "const double vs = (double)v_scale[slab + (j + 1) % L];"),
     ("int4_byte_index", "dot += widen_bf16(qrow[d]) * (ks * (double)int4_value(krow[d / 2], d & 1));",
      "dot += widen_bf16(qrow[d]) * (ks * (double)int4_value(krow[d % row_bytes], d & 1));"),
+    ("magnitude_without_abs", "return absv ? fabs(x) : x;", "return x;"),
+    ("magnitude_always_abs", "return absv ? fabs(x) : x;", "return fabs(x);"),
+    ("magnitude_int4_abs_of_code_only",
+     "o[d] += w[j] * vterm(vs * (double)int4_value(vrow[d / 2], d & 1), absv);",
+     "o[d] += w[j] * vs * vterm((double)int4_value(vrow[d / 2], d & 1), absv);"),
     ("split_chunk_off_by_one", "const int j1 = (j0 + chunk < L) ? j0 + chunk : L;",
      "const int j1 = (j0 + chunk < L) ? j0 + chunk - 1 : L;"),
 ]
