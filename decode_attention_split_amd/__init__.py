@@ -6,9 +6,15 @@ device memory and the current HIP stream.  The functions carry the C names.
 
 If ``libdas.so`` has not been built, every call raises: there is no CPU
 fallback.
+
+Streams: every call launches on ``stream`` (default: torch's current
+stream).  Tensors a call allocates itself (workspace, out, lse) are created
+on that stream; inputs and caller-supplied outputs must be ready on it (the
+caller orders them, as with any torch work on a side stream).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -27,8 +33,8 @@ DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 
 EXPORTED = ("das_plan", "das_plan_kv", "das_decode_workspace_bytes", "das_decode_attention",
             "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
-            "das_decode_attention_int4", "das_split_kv_decode_int4", "das_decode_attention_paged", "das_lse_combine", "das_merge_attn_states",
-            "das_strerror")
+            "das_decode_attention_int4", "das_split_kv_decode_int4", "das_decode_attention_paged",
+            "das_lse_combine", "das_merge_attn_states", "das_strerror")
 
 _lib = None
 
@@ -124,6 +130,14 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the tensors a call allocates itself (workspace, out,
+    lse) are created: on the stream the kernels run on, so that their
+    zero-fill is ordered before the launch and the caching allocator reuses
+    their memory only behind work on that stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _decode_shapes(q, k_cache, v_cache, seq_lens, kv_format: int = DAS_BF16):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         if not t.is_cuda:
@@ -153,13 +167,13 @@ def _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse):
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (B, Hq, D) \
-            or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 or bfloat16 [B,Hq,D] tensor")
+            or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 or bfloat16 [B,Hq,D] tensor on q's device")
     if lse_out is None and with_lse:
         lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse_out is not None and (lse_out.dtype != torch.float32 or lse_out.shape != (B, Hq)
-                                or not lse_out.is_contiguous()):
-        raise ValueError("lse_out must be a contiguous float32 [B,Hq] tensor")
+                                or not lse_out.is_contiguous() or lse_out.device != q.device):
+        raise ValueError("lse_out must be a contiguous float32 [B,Hq] tensor on q's device")
     return out, lse_out
 
 
@@ -174,8 +188,9 @@ def _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace):
 def _run_decode(fn_name, q, k_cache, v_cache, seq_lens, scale, out, lse_out, out_dtype,
                 num_splits, workspace, stream, with_lse):
     B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens)
-    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
-    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
+    with _on(stream):
+        out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+        workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
     dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
     fn = getattr(load_library(), fn_name)
     _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, Smax, D,
@@ -206,8 +221,9 @@ def _run_decode_fp8(fn_name, q, k_cache, v_cache, k_scale, v_scale, seq_lens, sc
     fmt = _SCALED[fn_name]
     B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens, fmt)
     _scales(k_scale, v_scale, _scale_shape(fmt, B, Hkv, Smax))
-    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
-    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
+    with _on(stream):
+        out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+        workspace, ws_bytes = _workspace(q, B, Hq, Hkv, Smax, D, num_splits, workspace)
     dtype_code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
     fn = getattr(load_library(), fn_name)
     _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
@@ -366,8 +382,9 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layo
     if kv_dtype == DAS_E4M3:
         _scales(k_scale, v_scale, (Hkv,))
     max_blocks = block_table.shape[1]
-    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
-    workspace, ws_bytes = _workspace(q, B, Hq, Hkv, max_blocks * P, D, num_splits, workspace)
+    with _on(stream):
+        out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
+        workspace, ws_bytes = _workspace(q, B, Hq, Hkv, max_blocks * P, D, num_splits, workspace)
     code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
     args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), kv_dtype, _ptr(k_scale), _ptr(v_scale),
             _ptr(block_table), max_blocks, P, num_pages, layout, _ptr(seq_lens), B, Hq, Hkv, D,
@@ -423,13 +440,21 @@ def das_merge_attn_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Ten
         raise ValueError("o_a and o_b must share dtype float32 or bfloat16")
     if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
         raise ValueError("lse must be float32")
-    for t in (o_a, o_b, lse_a, lse_b):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise ValueError("merge inputs must be contiguous device tensors")
-    if o_out is None:
-        o_out = torch.empty_like(o_a)
-    if lse_out is None:
-        lse_out = torch.empty_like(lse_a)
+    # the kernel writes rows * D elements of o_a's dtype and rows floats
+    if o_out is not None and (o_out.shape != o_a.shape or o_out.dtype != o_a.dtype
+                              or not o_out.is_contiguous()):
+        raise ValueError("o_out must be a contiguous tensor of o_a's shape and dtype")
+    if lse_out is not None and (lse_out.shape != lse_a.shape or lse_out.dtype != torch.float32
+                                or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must be a contiguous float32 tensor of lse_a's shape")
+    for t in (o_a, o_b, lse_a, lse_b) + tuple(t for t in (o_out, lse_out) if t is not None):
+        if not (t.is_cuda and t.is_contiguous()) or t.device != o_a.device:
+            raise ValueError("merge inputs and outputs must be contiguous tensors on one device")
+    with _on(stream):
+        if o_out is None:
+            o_out = torch.empty_like(o_a)
+        if lse_out is None:
+            lse_out = torch.empty_like(lse_a)
     D = o_a.shape[-1]
     rows = lse_a.numel()
     code = DAS_BF16 if o_a.dtype == torch.bfloat16 else DAS_F32

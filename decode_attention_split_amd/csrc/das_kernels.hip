@@ -14,9 +14,10 @@
 //     byte, so it is bound by HBM bandwidth.  Phase 1 streams K and V with
 //     16-byte loads in which 16 (D=128) or 8 (D=64) consecutive lanes cover
 //     one 256/128-byte row, so each wave-wide load covers whole rows.
-//   * For G in {4, 8} both products are real (small) matrix products and
+//   * For G in {4, 8, 16} both products are real (small) matrix products and
 //     run on the matrix cores (v_mfma_f32_16x16x32_bf16).  q.K^T is taken as
-//     K.q^T, 16 cached rows by the G query heads (padded to 16), so that each
+//     K.q^T, 16 cached rows by the G query heads (G = 16 fills the 16 columns,
+//     G = 4 and 8 pad them), so that each
 //     lane ends up holding one head's logits for eight rows -- exactly its
 //     slots of the A operand of p.V, with no data movement.  p is split into
 //     two bf16 halves (p = hi + lo to about 2^-18 relative), so p.V keeps

@@ -156,10 +156,10 @@ def test_many_split_workgroups_take_the_two_kernel_merge():
 
 
 def test_fused_merge_ignores_whatever_the_partial_slots_held():
-    """The fused merge reads a split's slot only once this call has written it:
-    every split clears its slots before it is counted.  Garbage, another
-    input's partials (left by the phase-1 entry point) or another shape's
-    leftovers in the partial area never reach the result."""
+    """The fused merge reads only the slots of this call's non-empty splits,
+    each written by this call before its workgroup is counted.  Garbage,
+    another input's partials (left by the phase-1 entry point) or another
+    shape's leftovers in the partial area never reach the result."""
     cfg = workloads.custom_config(2, 32, 8, 128, 5000)
     x = workloads.make_inputs(cfg, 10, seq_lens=(5000, 3100))
     y = workloads.make_inputs(cfg, 11, seq_lens=(4900, 5000))

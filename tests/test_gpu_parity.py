@@ -1,8 +1,9 @@
 """HIP path vs the fp64 oracle, element by element, on seeded inputs.
 
 Tolerances: fp32 output max|err| <= 5e-4, LSE max|err| <= 1e-4; bf16 output
-within 1 bf16 ulp of the oracle rounded to bf16 where |oracle| >= 2^-12 * S
-and within 2^-19 * S absolute below that, S = max(1, max |oracle|).  Rows past seq_lens are NaN in every cache."""
+within 1 bf16 ulp of the oracle rounded to bf16 where |oracle| >= 2^-5 * m
+and within 2^-14 * m + half an ulp everywhere, m = sum_j w_j |v_j| / Z per
+element (the oracle's magnitude form).  Rows past seq_lens are NaN in every cache."""
 import numpy as np
 import pytest
 import torch
@@ -52,12 +53,13 @@ def test_bf16_output(D, G):
     cfg = workloads.custom_config(3, 4 * G, 4, D, 2000, k_mult=4.0)
     x = workloads.make_inputs(cfg, 3000 + D + G, seq_lens=(2000, 1, 1234))
     ref_o, ref_l = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    mag = oracle.abs_attention(x.q, x.k, x.v, x.seq_lens, x.scale)
     t = upload(x)
     for ns in (0, 1):
         note(f"case bf16 D={D} G={G} num_splits={ns}")
         out, lse = run(x, ns, out_dtype=torch.bfloat16, tensors=t)
         assert out.dtype == torch.bfloat16
-        check_bf16(out, ref_o, f"bf16 D={D} G={G} ns={ns}")
+        check_bf16(out, ref_o, mag, f"bf16 D={D} G={G} ns={ns}")
         lse_err = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
         assert lse_err <= 1e-4
 
@@ -94,7 +96,8 @@ def test_named_config_full_size(idx):
     assert d_o <= 5e-4 and d_l <= 1e-4
     note(f"case full config {cfg.name}: bf16 output")
     outb, lseb = run(x, 0, out_dtype=torch.bfloat16, tensors=t)
-    check_bf16(outb, ref[0], f"{cfg.name} bf16 auto")
+    mag = oracle.abs_attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    check_bf16(outb, ref[0], mag, f"{cfg.name} bf16 auto")
     assert float(np.max(np.abs(lseb.cpu().numpy() - ref[1]))) <= 1e-4
     del t
     torch.cuda.empty_cache()
@@ -194,3 +197,27 @@ def test_group_of_16_at_a_405b_shape(fmt):
         note(f"case G=16 405B-shaped {fmt}: num_splits={ns}")
         out, lse = call(ns)
         check_f32(out, lse, *ref, f"G=16 {fmt} ns={ns}")
+
+
+def test_call_on_a_side_stream():
+    """A call on a stream other than torch's current one: the workspace, out
+    and lse the binding allocates are created on that stream (their zero-fill
+    ordered before the launch), while the current stream keeps allocating and
+    freeing memory; the results match the oracle every time."""
+    cfg = workloads.custom_config(2, 32, 8, 128, 6000)
+    x = workloads.make_inputs(cfg, 4400, seq_lens=(6000, 4321))
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    q, k, v, sl = upload(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # the inputs are ready on the side stream
+    results = []
+    for i in range(6):
+        # churn on the current stream: blocks freed here are reused at once
+        junk = torch.full((1 << 22,), float(i), device=q.device)
+        del junk
+        out, lse = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=7, stream=side)
+        results.append((out, lse))
+    side.synchronize()
+    torch.cuda.synchronize()
+    for i, (out, lse) in enumerate(results):
+        check_f32(out, lse, *ref, f"side stream call {i}")

@@ -236,6 +236,24 @@ def test_merge_argument_checks(lib):
     assert f(None, None, None, None, None, None, 0, 128, 0, None) == das.DAS_OK  # empty
 
 
+@pytest.mark.parametrize("bad", ["o_short", "o_dtype", "o_strided", "lse_short", "lse_dtype"])
+def test_merge_binding_rejects_mismatched_outputs(bad):
+    """Caller-supplied merge outputs must have the inputs' shape and dtype (the
+    kernel writes rows * D elements of o_a's dtype and rows floats): a smaller
+    or differently typed buffer is refused before anything is launched."""
+    import torch
+
+    o = torch.zeros(6, 128)
+    lse = torch.zeros(6)
+    outs = {"o_short": (torch.zeros(5, 128), None),
+            "o_dtype": (torch.zeros(6, 128, dtype=torch.bfloat16), None),
+            "o_strided": (torch.zeros(128, 6).t(), None),
+            "lse_short": (None, torch.zeros(5)),
+            "lse_dtype": (None, torch.zeros(6, dtype=torch.float64))}[bad]
+    with pytest.raises(ValueError, match="o_out|lse_out"):
+        das.das_merge_attn_states(o, lse, o.clone(), lse.clone(), o_out=outs[0], lse_out=outs[1])
+
+
 def test_binding_constants_match_the_header():
     import re
     text = open(os.path.join(ROOT, "include", "das.h")).read()
