@@ -9,7 +9,7 @@ import torch
 import decode_attention_split_amd as das
 import oracle
 import workloads
-from gpu_helpers import check_f32, dev, note, run, to_dev, upload
+from gpu_helpers import check_bf16, check_f32, dev, note, run, to_dev, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -121,22 +121,27 @@ def test_paged_table_entries_outside_the_pool_are_contained():
     check_f32(out[ok], lse[ok], ref_o[ok], ref_l[ok], "sequences with valid entries")
 
 
-@pytest.mark.parametrize("idx,P,layout", [(1, 64, HND), (3, 256, NHD)],
-                         ids=["gqa_32k_P64_HND", "varlen_b64_P256_NHD"])
+@pytest.mark.parametrize("idx,P,layout", [(1, 64, HND), (2, 256, HND), (3, 256, NHD),
+                                          (4, 128, NHD)],
+                         ids=["gqa_32k_P64_HND", "gqa_128k_P256_HND", "varlen_b64_P256_NHD",
+                              "ragged_b8_P128_NHD"])
 def test_paged_named_config_full_size(idx, P, layout):
-    """Named configs at full size in a paged pool, automatic plan; the oracle
-    covers every output (the B=64 batch: 16 of its sequences)."""
+    """Named configs at full size in a paged pool, automatic plan, against the
+    oracle over every output (the definition over the rows the generator
+    scattered into the pool), with fp32 and bf16 outputs."""
     cfg = workloads.CONFIGS[idx]
     note(f"case paged full config {cfg.name} P={P}: generating inputs")
     x = workloads.make_paged_inputs(cfg, 42 + idx, P, layout)
     t = upload_paged(x)
     note(f"case paged full config {cfg.name}: auto splits")
     out, lse = run_paged(x, 0, tensors=t)
-    B = len(x.base.seq_lens)
-    rows = np.arange(B) if B <= 16 else np.arange(0, B, 4)
-    note(f"case paged full config {cfg.name}: oracle on {len(rows)} batch rows")
-    ref_o, ref_l = oracle.attention(x.base.q[rows], x.base.k[rows], x.base.v[rows],
-                                    x.base.seq_lens[rows], x.base.scale)
-    check_f32(out[rows], lse[rows], ref_o, ref_l, f"paged {cfg.name}")
+    note(f"case paged full config {cfg.name}: oracle on all {len(x.base.seq_lens)} batch rows")
+    ref_o, ref_l = oracle.attention(x.base.q, x.base.k, x.base.v, x.base.seq_lens, x.base.scale)
+    check_f32(out, lse, ref_o, ref_l, f"paged {cfg.name}")
+    note(f"case paged full config {cfg.name}: bf16 output")
+    outb, lseb = run_paged(x, 0, out_dtype=torch.bfloat16, tensors=t)
+    mag = oracle.abs_attention(x.base.q, x.base.k, x.base.v, x.base.seq_lens, x.base.scale)
+    check_bf16(outb, ref_o, mag, f"paged {cfg.name} bf16")
+    assert torch.equal(lseb, lse), "lse differs between output modes"
     del t
     torch.cuda.empty_cache()
