@@ -6,14 +6,19 @@ kv-head), a single kernel launch; on grids of more than 4 split workgroups
 per CU phase 2 runs as a second, small kernel) over the synthetic workload,
 with every input already resident in HBM.  K/V are rotated over several
 copies so that repeated steps read from HBM rather than from the 256 MB
-last-level cache.
+last-level cache.  The default workload is the largest named config that
+fits one GPU: the batched variable-length GQA decode (B=64, Hq=32, Hkv=8,
+D=128, lengths U[512, 16384], 2.36 GB of K/V per call).
 
 Prints one JSON line on stdout.  Also reports the achieved algorithmic HBM
 bandwidth of the call's kernels against the MI355X peak, measured with HIP
 events on the launch stream around the timed launches; for reference only,
 the same calls replayed from one HIP graph and the median of calls issued
-one at a time after a cache flush; and the fp64 CPU oracle's throughput on a
-bounded sample of the same workload (the reported CPU baseline).
+one at a time after a cache flush; the fp64 CPU oracle's throughput on a
+bounded sample of the same workload (the reported CPU baseline); and, in
+``config.per_config``, every named config timed in the same process
+(automatic plan with fp32 and bf16 output, and one split).  Progress goes
+to stderr.
 """
 from __future__ import annotations
 
@@ -49,7 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="index into workloads.CONFIGS")
+    ap.add_argument("--config", type=int, default=3,
+                    help="index into workloads.CONFIGS (default 3: the batched varlen GQA "
+                         "decode, B=64, the largest config)")
     ap.add_argument("--splits", type=int, default=0, help="0 = automatic plan")
     ap.add_argument("--hq", type=int, default=0,
                     help="query heads instead of the config's own (same kv-heads, lengths and "
@@ -74,6 +81,12 @@ def parse():
                     help="decode: the decode-attention call (the headline); merge: "
                          "das_merge_attn_states alone, at one decode step's rows and at a "
                          "bandwidth-sized call")
+    ap.add_argument("--table", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time every named config (bf16 K/V) in this process: automatic "
+                         "plan with fp32 and bf16 output, and one split")
+    ap.add_argument("--table-steps", type=int, default=50,
+                    help="back-to-back launches timed per table row")
+    ap.add_argument("--table-warmup", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -232,6 +245,200 @@ def cpu_baseline(x, target_s: float):
             "cpu": cpu_model()}
 
 
+def fused_merge(B: int, Hkv: int, ns: int, cus: int) -> str:
+    """How das_decode_attention runs phase 2 for this plan: in the decode
+    kernel (the last workgroup of each (b, kv-head) merges), as a second
+    kernel (lse_combine: more than 4 split workgroups per CU, or more
+    (b, kv-head) pairs than the library's 65536 arrival counters), or not at
+    all (a single split writes the output directly)."""
+    if ns <= 1:
+        return "none (one split)"
+    if B * Hkv <= 65536 and B * Hkv * ns <= 4 * cus:
+        return "fused"
+    return "two kernels"
+
+
+class Workload:
+    """One config's inputs resident in HBM (K/V rotated over several copies so
+    that back-to-back calls read from HBM, not from the last-level cache),
+    with prepared library calls."""
+
+    def __init__(self, args, config: int, kv_dtype: str = "bf16", paged: int = 0,
+                 paged_layout: str = "hnd", hq: int = 0, copies: int = 0, x=None):
+        import numpy as np
+        import torch
+
+        import decode_attention_split_amd as das
+        import workloads
+
+        self.torch, self.das = torch, das
+        dev = torch.device("cuda:0")
+        cfg = workloads.CONFIGS[config]
+        if hq:
+            import dataclasses
+            cfg = dataclasses.replace(cfg, name=f"{cfg.name}_hq{hq}", Hq=hq,
+                                      description=f"{cfg.description}, Hq={hq} instead")
+        self.cfg = cfg
+        self.kv_dtype = kv_dtype
+        int4 = kv_dtype == "int4"
+        fp8 = kv_dtype == "fp8"
+        self.quant = quant = fp8 or int4      # codes plus fp32 scales
+        self.paged = None
+        if paged:
+            if int4:
+                sys.exit("bench.py: there is no paged INT4 cache")
+            layout = workloads.PAGED_HND if paged_layout == "hnd" else workloads.PAGED_NHD
+            self.paged = workloads.make_paged_inputs(cfg, 42 + config, paged, layout, fp8=fp8)
+            x = self.paged.base
+        elif x is None:
+            if int4:
+                x = workloads.make_int4_inputs(cfg, 42 + config)
+            else:
+                x = (workloads.make_fp8_inputs if fp8 else workloads.make_inputs)(cfg, 42 + config)
+        self.x = x
+        B, Hq, D = x.q.shape
+        Hkv, Smax = x.k.shape[1], x.k.shape[2]
+        self.kv_bytes = x.kv_bytes
+        if self.paged is not None:
+            # the paged plan: Smax = max_blocks * page size, chunks rounded up to whole pages
+            Smax = self.paged.block_table.shape[1] * self.paged.page_size
+        self.B, self.Hq, self.Hkv, self.Smax, self.D = B, Hq, Hkv, Smax, D
+        self.kv_code = das.DAS_INT4 if int4 else (das.DAS_E4M3 if fp8 else das.DAS_BF16)
+        self.cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        self.q = up(x.q)
+        self.sl = torch.from_numpy(x.seq_lens).to(dev)
+        k_scale = v_scale = None
+        alloc = x.k.nbytes + x.v.nbytes
+        if quant:
+            k_scale = torch.from_numpy(x.k_scale).to(dev)
+            v_scale = torch.from_numpy(x.v_scale).to(dev)
+            if int4:
+                alloc += x.k_scale.nbytes + x.v_scale.nbytes
+        src_k, src_v = ((self.paged.k_pool, self.paged.v_pool) if self.paged is not None
+                        else (x.k, x.v))
+        if quant:
+            k0, v0 = torch.from_numpy(src_k).to(dev), torch.from_numpy(src_v).to(dev)
+        else:
+            k0, v0 = up(src_k), up(src_v)
+        self.table = None
+        if self.paged is not None:
+            alloc = self.paged.k_pool.nbytes + self.paged.v_pool.nbytes
+            self.table = torch.from_numpy(self.paged.block_table).to(dev)
+        self.copies = copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
+        self.ks, self.vs = [k0], [v0]
+        self.kss, self.vss = [k_scale], [v_scale]
+        for _ in range(self.copies - 1):
+            self.ks.append(k0.clone())
+            self.vs.append(v0.clone())
+            # an INT4 cache's row scales are streamed with its codes: rotate them too
+            self.kss.append(k_scale.clone() if int4 else k_scale)
+            self.vss.append(v_scale.clone() if int4 else v_scale)
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.ws = {}
+
+    def plan(self, splits: int):
+        ns, chunk = self.das.das_plan_kv(self.kv_code, self.B, self.Hkv, self.Hq // self.Hkv,
+                                         self.Smax, self.D, splits)
+        if self.paged is not None and chunk % self.paged.page_size:
+            P = self.paged.page_size
+            chunk = -(-chunk // P) * P
+            ns = -(-self.Smax // chunk)
+        return ns, chunk
+
+    def workspace(self, splits: int):
+        if splits not in self.ws:
+            n = self.das.das_decode_workspace_bytes(self.B, self.Hq, self.Hkv, self.Smax, self.D,
+                                                    splits)
+            # zero-filled: the workspace starts with the library's arrival counters
+            self.ws[splits] = self.torch.zeros(max(n, 16), dtype=self.torch.uint8,
+                                               device=self.q.device)
+        return self.ws[splits]
+
+    def calls(self, splits: int, out, lse, stream=None):
+        """One prepared decode-attention call per K/V copy."""
+        das, ws = self.das, self.workspace(splits)
+        if self.paged is not None:
+            return [das.prepare_decode_paged(self.q, self.ks[c], self.vs[c], self.table, self.sl,
+                                             self.x.scale, self.paged.page_size,
+                                             self.paged.layout, out, lse, splits, ws,
+                                             stream=stream, k_scale=self.k_scale,
+                                             v_scale=self.v_scale)
+                    for c in range(self.copies)]
+        if self.quant:
+            name = ("das_decode_attention_int4" if self.kv_dtype == "int4"
+                    else "das_decode_attention_fp8")
+            return [das.prepare_decode(name, self.q, self.ks[c], self.vs[c], self.sl,
+                                       self.x.scale, out, lse, splits, ws, stream=stream,
+                                       k_scale=self.kss[c], v_scale=self.vss[c])
+                    for c in range(self.copies)]
+        return [das.prepare_decode("das_decode_attention", self.q, self.ks[c], self.vs[c],
+                                   self.sl, self.x.scale, out, lse, splits, ws, stream=stream)
+                for c in range(self.copies)]
+
+    def outputs(self, out_dtype: str):
+        torch = self.torch
+        dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+        return (torch.empty((self.B, self.Hq, self.D), dtype=dt, device=self.q.device),
+                torch.empty((self.B, self.Hq), dtype=torch.float32, device=self.q.device))
+
+    def event_us(self, calls, n: int, warmup: int) -> float:
+        """Average µs per call over n back-to-back launches, from a pair of HIP
+        events on the launch stream (torch's current stream)."""
+        torch = self.torch
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            calls[(warmup + i) % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    def row(self, splits: int, out_dtype: str, n: int, warmup: int) -> dict:
+        """One line of the per-config table."""
+        out, lse = self.outputs(out_dtype)
+        us = self.event_us(self.calls(splits, out, lse), n, warmup)
+        ns, chunk = self.plan(splits)
+        gbs = self.kv_bytes / (us * 1e-6) / 1e9
+        return {"workload": self.cfg.name, "splits": "auto" if splits == 0 else splits,
+                "plan": f"{ns} x {chunk}", "merge": fused_merge(self.B, self.Hkv, ns, self.cus),
+                "out_dtype": out_dtype, "kv_bytes": self.kv_bytes, "us_per_call": round(us, 2),
+                "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "launches": n}
+
+
+def per_config_table(args, headline: "Workload") -> list:
+    """Every named config (bf16 K/V) in this process: the automatic plan with
+    fp32 output, the same with bf16 output, and one split (the unsplit
+    kernel the pages start from) -- µs per call by HIP events over
+    args.table_steps back-to-back launches."""
+    import torch
+
+    import workloads
+
+    rows = []
+    for idx in range(len(workloads.CONFIGS)):
+        if headline is not None and idx == args.config and headline.kv_dtype == "bf16" \
+                and headline.paged is None and not args.hq:
+            w = headline
+        else:
+            w = Workload(args, idx)
+        for splits, out_dtype in ((0, "f32"), (0, "bf16"), (1, "f32")):
+            rows.append(w.row(splits, out_dtype, args.table_steps, args.table_warmup))
+        print(f"bench: table {w.cfg.name} done", file=sys.stderr, flush=True)
+        if w is not headline:
+            del w
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -251,97 +458,22 @@ def main():
     import torch
 
     import decode_attention_split_amd as das
-    import workloads
 
     das.load_library()
-    dev = torch.device("cuda:0")
-    cfg = workloads.CONFIGS[args.config]
-    if args.hq:
-        import dataclasses
-        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_hq{args.hq}", Hq=args.hq,
-                                  description=f"{cfg.description}, Hq={args.hq} instead")
-    int4 = args.kv_dtype == "int4"
-    fp8 = args.kv_dtype == "fp8"
-    quant = fp8 or int4      # codes plus fp32 scales
-    paged = None
-    if args.paged:
-        if int4:
-            sys.exit("bench.py: there is no paged INT4 cache")
-        layout = workloads.PAGED_HND if args.paged_layout == "hnd" else workloads.PAGED_NHD
-        paged = workloads.make_paged_inputs(cfg, 42 + args.config, args.paged, layout, fp8=fp8)
-        x = paged.base
-    elif int4:
-        x = workloads.make_int4_inputs(cfg, 42 + args.config)
-    else:
-        x = (workloads.make_fp8_inputs if fp8 else workloads.make_inputs)(cfg, 42 + args.config)
-    B, Hq, D = x.q.shape
-    Hkv, Smax = x.k.shape[1], x.k.shape[2]
-    kv_bytes = x.kv_bytes
-    if paged is not None:
-        # the paged plan: Smax = max_blocks * page size, chunks rounded up to whole pages
-        Smax = paged.block_table.shape[1] * paged.page_size
-    kv_code = das.DAS_INT4 if int4 else (das.DAS_E4M3 if fp8 else das.DAS_BF16)
-    ns, chunk = das.das_plan_kv(kv_code, B, Hkv, Hq // Hkv, Smax, D, args.splits)
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    if paged is not None and chunk % paged.page_size:
-        chunk = -(-chunk // paged.page_size) * paged.page_size
-        ns = -(-Smax // chunk)
+    w = Workload(args, args.config, args.kv_dtype, args.paged, args.paged_layout, args.hq,
+                 args.copies)
+    cfg, x = w.cfg, w.x
+    B, Hq, Hkv, Smax, D = w.B, w.Hq, w.Hkv, w.Smax, w.D
+    kv_bytes = w.kv_bytes
+    ns, chunk = w.plan(args.splits)
+    out, lse = w.outputs(args.out_dtype)
+    calls = w.calls(args.splits, out, lse)
+    copies = w.copies
 
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    q = up(x.q)
-    sl = torch.from_numpy(x.seq_lens).to(dev)
-    alloc = x.k.nbytes + x.v.nbytes
-    copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
-    k_scale = v_scale = None
-    if quant:
-        k_scale, v_scale = torch.from_numpy(x.k_scale).to(dev), torch.from_numpy(x.v_scale).to(dev)
-        if int4:
-            alloc += x.k_scale.nbytes + x.v_scale.nbytes
-            copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
-    src_k, src_v = (paged.k_pool, paged.v_pool) if paged is not None else (x.k, x.v)
-    if quant:
-        k0, v0 = torch.from_numpy(src_k).to(dev), torch.from_numpy(src_v).to(dev)
-    else:
-        k0, v0 = up(src_k), up(src_v)
-    if paged is not None:
-        alloc = paged.k_pool.nbytes + paged.v_pool.nbytes
-        copies = args.copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
-        table = torch.from_numpy(paged.block_table).to(dev)
-    ks, vs = [k0], [v0]
-    kss, vss = [k_scale], [v_scale]
-    for _ in range(copies - 1):
-        ks.append(k0.clone())
-        vs.append(v0.clone())
-        # an INT4 cache's row scales are streamed with its codes: rotate them too
-        kss.append(k_scale.clone() if int4 else k_scale)
-        vss.append(v_scale.clone() if int4 else v_scale)
-    out_dtype = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-    out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    ws = torch.zeros(max(das.das_decode_workspace_bytes(B, Hq, Hkv, Smax, D, args.splits), 16),
-                     dtype=torch.uint8, device=dev)   # zero-filled: starts with arrival counters
-
-    # One prepared decode-attention call per K/V copy.  It is a single kernel
-    # launch: phase 1 plus the fused phase-2 merge by the last workgroup of
-    # each (b, kv-head).
-    def make_calls(stream=None):
-        if paged is not None:
-            return [das.prepare_decode_paged(q, ks[c], vs[c], table, sl, x.scale, paged.page_size,
-                                             paged.layout, out, lse, args.splits, ws, stream=stream,
-                                             k_scale=k_scale, v_scale=v_scale)
-                    for c in range(copies)]
-        if quant:
-            name = "das_decode_attention_int4" if int4 else "das_decode_attention_fp8"
-            return [das.prepare_decode(name, q, ks[c], vs[c], sl, x.scale, out, lse, args.splits,
-                                       ws, stream=stream, k_scale=kss[c], v_scale=vss[c])
-                    for c in range(copies)]
-        return [das.prepare_decode("das_decode_attention", q, ks[c], vs[c], sl, x.scale, out, lse,
-                                   args.splits, ws, stream=stream) for c in range(copies)]
-
-    calls = make_calls()
-
+    # The timed region: exactly K steps, bracketed by synchronizes.  Each step
+    # is one decode-attention call (one kernel launch, two where phase 2 runs
+    # as its own kernel) on torch's current stream, so the events around the K
+    # back-to-back launches give the call's average duration on the GPU.
     for i in range(args.warmup):
         calls[i % copies]()
     torch.cuda.synchronize()
@@ -356,12 +488,11 @@ def main():
     ev_end.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # Each step is one kernel launch on this stream, so the events around the
-    # K back-to-back launches give that kernel's average launch duration.
     kernel_ms = ev_start.elapsed_time(ev_end) / K
     ms_per_step = elapsed / K * 1e3
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (kernel_ms * 1e-3) / 1e9
+    print(f"bench: timed {K} steps of {cfg.name}", file=sys.stderr, flush=True)
 
     # For reference only (not `value`): the same K calls captured in one HIP
     # graph and replayed, as a serving engine issues a decode step.  The
@@ -369,7 +500,7 @@ def main():
     graph_us = None
     if args.graph:
         gs = torch.cuda.Stream()
-        gcalls = make_calls(gs)
+        gcalls = w.calls(args.splits, out, lse, stream=gs)
         graph = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=gs):
@@ -391,7 +522,7 @@ def main():
     # pair of events; the median of 100.
     isolated_us = None
     if args.isolated:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=out.device)
         n = 100
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
@@ -405,6 +536,9 @@ def main():
         isolated_us = round(sorted(a.elapsed_time(b) for a, b in evs)[n // 2] * 1e3, 2)
         del flush
 
+    quant, paged = w.quant, w.paged
+    fp8, int4 = args.kv_dtype == "fp8", args.kv_dtype == "int4"
+    merge = fused_merge(B, Hkv, ns, w.cus)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -425,33 +559,40 @@ def main():
             "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "Smax": Smax,
             "tokens": int(x.seq_lens.astype(np.int64).sum()),
             "kv_bytes": kv_bytes,
-            "num_splits": ns, "chunk": chunk,
+            "num_splits": ns, "chunk": chunk, "merge": merge,
             "out_dtype": args.out_dtype,
             "kv_dtype": args.kv_dtype,
             "paged": ({"page_size": paged.page_size, "layout": args.paged_layout}
                       if paged is not None else None),
             "kv_copies_rotated": copies,
+            # value = kv_bytes / (host wall clock over the K timed steps, from
+            # before the first launch to after the final synchronize) / K
+            "value_clock": "host wall clock over the timed steps, incl. the final synchronize",
             "us_per_call": round(ms_per_step * 1e3, 2),
+            "us_per_call_hip_events": round(kernel_ms * 1e3, 3),
             "us_per_call_graph_replay": graph_us,
             "us_per_call_isolated_median": isolated_us,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         },
         "roofline": {
             "bound": "hbm",
-            # phase 2 runs fused unless the plan has more than 4 split
-            # workgroups per CU or more (b, kv-head) pairs than counter slots
-            "kernel": ("split_kv_decode" if B * Hkv <= 65536 and B * Hkv * ns <= 4 * cus
-                       else "split_kv_decode + lse_combine"),
+            "kernel": ("split_kv_decode + lse_combine" if merge == "two kernels"
+                       else "split_kv_decode"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (quant or paged is not None) else measured_traffic(cfg.name, ns),
+            "traffic": None if (quant or paged is not None or args.hq or args.splits
+                                or args.out_dtype != "f32") else measured_traffic(cfg.name, ns),
             "kernel_us": round(kernel_ms * 1e3, 3),
         },
     }
     if args.cpu_seconds > 0 and not quant and paged is None:
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        print("bench: cpu baseline done", file=sys.stderr, flush=True)
+    if args.table:
+        del calls
+        result["config"]["per_config"] = per_config_table(args, w)
     print(json.dumps(result), flush=True)
 
 

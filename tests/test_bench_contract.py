@@ -19,10 +19,31 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+def test_default_workload_is_the_largest_config_with_the_table():
+    """With no flags the headline is the batched varlen B=64 config (the
+    largest that fits one GPU) and every named config is timed beside it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+
+    old = sys.argv
+    sys.argv = ["bench.py"]
+    try:
+        args = bench.parse()
+    finally:
+        sys.argv = old
+    assert workloads.CONFIGS[args.config].name == "gqa_b64_h32x8_d128_varlen16k"
+    assert args.table and args.gpus == 1 and args.splits == 0 and args.out_dtype == "f32"
+    assert bench.fused_merge(64, 8, 5, 256) == "two kernels"
+    assert bench.fused_merge(1, 8, 24, 256) == "fused"
+    assert bench.fused_merge(1, 8, 1, 256) == "none (one split)"
+
+
 @pytest.mark.gpu
 def test_bench_prints_one_json_line_with_the_contract_fields():
     r = subprocess.run([sys.executable, BENCH, "--config", "0", "--steps", "5", "--warmup", "2",
-                        "--cpu-seconds", "0.5"], capture_output=True, text=True, timeout=300)
+                        "--cpu-seconds", "0.5", "--no-table"], capture_output=True, text=True,
+                       timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1
