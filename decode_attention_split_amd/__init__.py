@@ -34,7 +34,9 @@ DAS_WORKSPACE_COUNTER_BYTES = 65536 * 4
 EXPORTED = ("das_plan", "das_plan_kv", "das_decode_workspace_bytes", "das_decode_attention",
             "das_split_kv_decode", "das_decode_attention_fp8", "das_split_kv_decode_fp8",
             "das_decode_attention_int4", "das_split_kv_decode_int4", "das_decode_attention_paged",
-            "das_lse_combine", "das_merge_attn_states", "das_strerror")
+            "das_lse_combine", "das_merge_attn_states", "das_decode_attention_noalloc",
+            "das_strerror")
+DAS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -75,6 +77,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                i32, i32, i32, ctypes.c_float, p, i32, p, i32, p,
                                                sz, p]
     lib.das_decode_attention_paged.restype = ctypes.c_int
+    lib.das_decode_attention_noalloc.argtypes = [p, p, p, p, i32, i32, i32, i32, i32,
+                                                 ctypes.c_float, p, i32, p, i32, p]
+    lib.das_decode_attention_noalloc.restype = ctypes.c_int
     lib.das_lse_combine.argtypes = [p, i32, i32, i32, i32, i32, i32, p, sz, p, i32, p, p]
     lib.das_lse_combine.restype = ctypes.c_int
     lib.das_merge_attn_states.argtypes = [p, p, p, p, p, p, i64, i32, i32, p]
@@ -298,6 +303,22 @@ def das_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     """Decode attention; returns (out [B,Hq,D], lse [B,Hq] or None)."""
     out, lse_out, _ = _run_decode("das_decode_attention", q, k_cache, v_cache, seq_lens, scale,
                                   out, lse_out, out_dtype, num_splits, workspace, stream, with_lse)
+    return out, lse_out
+
+
+def das_decode_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                                 lse_out: Optional[torch.Tensor] = None, num_splits: int = 0,
+                                 stream=None):
+    """das_decode_attention with the library's static workspace: the caller
+    passes its outputs (nothing is allocated on this path); returns (out, lse)."""
+    B, Hq, Hkv, Smax, D = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out.dtype, False)
+    code = DAS_BF16 if out.dtype == torch.bfloat16 else DAS_F32
+    _check(load_library().das_decode_attention_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, Smax, D, float(scale),
+        _ptr(out), code, _ptr(lse_out), int(num_splits), _stream(stream)),
+        "das_decode_attention_noalloc")
     return out, lse_out
 
 

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdas.so")
-SOURCES = [os.path.join(CSRC, "das_kernels.hip"), os.path.join(CSRC, "das_api.cpp")]
+SOURCES = [os.path.join(CSRC, "das_kernels.hip"), os.path.join(CSRC, "das_api.cpp"),
+           os.path.join(CSRC, "das_noalloc.hip")]
 HEADERS = [os.path.join(ROOT, "include", "das.h"), os.path.join(CSRC, "das_internal.h")]
 
 

@@ -36,7 +36,8 @@
  *   - The caller owns all memory.  The library never allocates, frees,
  *     synchronises the device or copies device memory to the host, so every
  *     call can be recorded into a HIP graph.  It caches only the compute-unit
- *     count of each device it has seen.
+ *     count of each device it has seen (and, for das_decode_attention_noalloc,
+ *     the address of its static workspace on each device).
  *   - Arguments are checked on the host before anything is launched.  On a
  *     failed check the call returns a negative status, launches nothing and
  *     leaves every output untouched.  A launch error returns DAS_ELAUNCH.
@@ -320,6 +321,29 @@ int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
 int das_merge_attn_states(const void* o_a, const float* lse_a, const void* o_b,
                           const float* lse_b, void* o_out, float* lse_out, int64_t rows,
                           int32_t D, int32_t o_dtype, void* stream);
+
+/*
+ * das_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without workspace and workspace_bytes, the
+ * same plan, kernels and results.  Its workspace is a static device array
+ * of DAS_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; the call itself allocates and frees nothing.
+ * The first call on a device looks the array up and zeroes its arrival
+ * counters (a small fill kernel on `stream`, ahead of the call's kernels).
+ *   Returns DAS_EWORKSPACE, launching nothing, when the shape and split
+ *   request need more than DAS_NOALLOC_SCRATCH_BYTES of workspace
+ *   (das_decode_workspace_bytes tells); otherwise as das_decode_attention.
+ *   Every call on one GPU shares that GPU's array, and it keeps the last
+ *   call's contents: calls that overlap on one GPU (concurrent streams, or
+ *   host threads) race and give wrong results; serialise them.
+ */
+#define DAS_NOALLOC_SCRATCH_BYTES 67108864 /* 64 MiB */
+int das_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                 int32_t Smax, int32_t D, float scale, void* out,
+                                 int32_t out_dtype, float* lse_out, int32_t num_splits,
+                                 void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* das_strerror(int status);
