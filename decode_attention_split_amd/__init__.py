@@ -372,19 +372,25 @@ def das_split_kv_decode_int4(q, k_cache, v_cache, k_scale, v_scale, seq_lens, sc
 
 
 def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layout, k_scale,
-                v_scale, out, lse_out, out_dtype, num_splits, workspace, stream, with_lse):
+                v_scale, out, lse_out, out_dtype, num_splits, workspace, stream, with_lse,
+                kv_dtype=None):
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
                     ("block_table", block_table), ("seq_lens", seq_lens)):
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
     if q.dtype != torch.bfloat16 or q.dim() != 3:
         raise ValueError("q must be bfloat16 [B,Hq,D]")
-    if k_pool.dtype == torch.bfloat16:
-        kv_dtype = DAS_BF16
-    elif k_pool.dtype in (torch.uint8, torch.float8_e4m3fn):
-        kv_dtype = DAS_E4M3
-    else:
-        raise ValueError("page pools must be bfloat16, or E4M3 codes (uint8 / float8_e4m3fn)")
+    if kv_dtype is None:   # bf16 or E4M3 from the pool's dtype; INT4 must be named
+        if k_pool.dtype == torch.bfloat16:
+            kv_dtype = DAS_BF16
+        elif k_pool.dtype in (torch.uint8, torch.float8_e4m3fn):
+            kv_dtype = DAS_E4M3
+        else:
+            raise ValueError("page pools must be bfloat16, or E4M3 codes (uint8 / float8_e4m3fn)")
+    want = {DAS_BF16: (torch.bfloat16,), DAS_E4M3: (torch.uint8, torch.float8_e4m3fn),
+            DAS_INT4: (torch.uint8,)}.get(kv_dtype)
+    if want is None or k_pool.dtype not in want:
+        raise ValueError("page pool dtype does not match kv_dtype")
     if v_pool.dtype != k_pool.dtype or v_pool.shape != k_pool.shape or k_pool.dim() != 4:
         raise ValueError("k_pool and v_pool must share one 4-d shape and dtype")
     B, Hq, D = q.shape
@@ -394,7 +400,7 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layo
         num_pages, P, Hkv, Dk = k_pool.shape
     else:
         raise ValueError("layout must be DAS_PAGED_HND or DAS_PAGED_NHD")
-    if P != page_size or Dk != D:
+    if P != page_size or Dk != (D // 2 if kv_dtype == DAS_INT4 else D):
         raise ValueError("pool shape disagrees with page_size or D")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be int32 [B, max_blocks]")
@@ -402,6 +408,8 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layo
         raise ValueError("seq_lens must be int32 [B]")
     if kv_dtype == DAS_E4M3:
         _scales(k_scale, v_scale, (Hkv,))
+    elif kv_dtype == DAS_INT4:   # row-scale pools laid out like the code pools
+        _scales(k_scale, v_scale, k_pool.shape[:3])
     max_blocks = block_table.shape[1]
     with _on(stream):
         out, lse_out = _outputs(q, B, Hq, D, out, lse_out, out_dtype, with_lse)
@@ -418,23 +426,25 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layo
 def das_decode_attention_paged(q, k_pool, v_pool, block_table, seq_lens, scale, page_size,
                                layout=0, k_scale=None, v_scale=None, out=None, lse_out=None,
                                out_dtype=torch.float32, num_splits=0, workspace=None, stream=None,
-                               with_lse=True):
-    """Decode attention over a paged cache (bf16 or E4M3 page pools, int32 block
-    table [B, max_blocks]); returns (out, lse)."""
+                               with_lse=True, kv_dtype=None):
+    """Decode attention over a paged cache (bf16, E4M3 or -- with
+    kv_dtype=DAS_INT4 and row-scale pools shaped like the code pools minus D --
+    INT4 page pools; int32 block table [B, max_blocks]); returns (out, lse)."""
     args, _, out, lse_out = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale,
                                         page_size, layout, k_scale, v_scale, out, lse_out,
-                                        out_dtype, num_splits, workspace, stream, with_lse)
+                                        out_dtype, num_splits, workspace, stream, with_lse,
+                                        kv_dtype)
     _check(load_library().das_decode_attention_paged(*args), "das_decode_attention_paged")
     return out, lse_out
 
 
 def prepare_decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale, page_size, layout,
                          out, lse_out, num_splits, workspace, stream=None, k_scale=None,
-                         v_scale=None) -> "PreparedCall":
+                         v_scale=None, kv_dtype=None) -> "PreparedCall":
     """Prepared das_decode_attention_paged call (same checks once)."""
     args, keep, _, _ = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, page_size,
                                    layout, k_scale, v_scale, out, lse_out, out.dtype, num_splits,
-                                   workspace, stream, lse_out is not None)
+                                   workspace, stream, lse_out is not None, kv_dtype)
     return PreparedCall("das_decode_attention_paged", args, keep)
 
 

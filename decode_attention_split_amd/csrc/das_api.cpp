@@ -58,10 +58,6 @@ bool supported_dims(int D, int G) {
   return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-// GQA groups of 16 heads need a wave's end-of-stream state (16 heads x D
-// floats) to fit in its tile region, which the INT4 tiles are too small for.
-bool format_supports_group(int format, int G) { return format != das::kKvInt4 || G <= 8; }
-
 int device_cus(int32_t num_cus, int* out) {
   if (num_cus > 0) {
     *out = num_cus;
@@ -207,20 +203,25 @@ int run_phase1(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   a.k_scale = kv.k_scale;
   a.v_scale = kv.v_scale;
   if (kv.paged()) {
-    const int E = (int)kv.row_bytes(D) / D;   // bf16 or E4M3 pools
+    const int64_t R = kv.row_bytes(D);   // bytes of one row of one kv-head
     int shift = 0;
     while ((1 << shift) < kv.page_size) ++shift;
     a.block_table = kv.block_table;
     a.max_blocks = kv.max_blocks;
     a.page_shift = shift;
     a.num_pages = kv.num_pages;
-    a.page_bytes = (int64_t)kv.page_size * Hkv * D * E;
+    a.page_bytes = (int64_t)kv.page_size * Hkv * R;
+    a.scale_page_stride = kv.page_size * Hkv;   // INT4 row-scale pools
     if (kv.layout == DAS_PAGED_HND) {
-      a.row_stride = D * E;
-      a.head_stride = kv.page_size * D * E;
+      a.row_stride = (int32_t)R;
+      a.head_stride = (int32_t)(kv.page_size * R);
+      a.scale_head_stride = kv.page_size;
+      a.scale_row_stride = 1;
     } else {
-      a.row_stride = Hkv * D * E;
-      a.head_stride = D * E;
+      a.row_stride = (int32_t)(Hkv * R);
+      a.head_stride = (int32_t)R;
+      a.scale_head_stride = 1;
+      a.scale_row_stride = Hkv;
     }
   }
   a.seq_lens = seq_lens;
@@ -288,7 +289,6 @@ int split_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32_
   const int rc = check_decode(q, kv.k, kv.v, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype,
                               num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c);
   if (rc != DAS_OK) return rc;
-  if (!format_supports_group(kv.format, c.G)) return DAS_ENOTSUP;
   return run_phase1(q, kv, seq_lens, B, Hq, Hkv, Smax, D, scale, out, out_dtype, lse_out,
                     workspace, c, false, static_cast<hipStream_t>(stream));
 }
@@ -304,7 +304,6 @@ int decode_impl(const void* q, const KvCache& kv, const int32_t* seq_lens, int32
                               num_splits, workspace, workspace_bytes, true, kv.row_bytes(D), &c,
                               kv.page_size, wgs_for_format(kv.format));
   if (rc != DAS_OK) return rc;
-  if (!format_supports_group(kv.format, c.G)) return DAS_ENOTSUP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // One launch: the last workgroup of each (b, kv-head) merges the splits.
   // Every split workgroup then ends with a store-completion wait and a
@@ -343,7 +342,6 @@ int das_plan_kv(int32_t kv_dtype, int32_t B, int32_t Hkv, int32_t G, int32_t Sma
     case DAS_INT4: format = das::kKvInt4; break;
     default: return DAS_EINVAL;
   }
-  if (!format_supports_group(format, G)) return DAS_ENOTSUP;
   return plan_impl(B, Hkv, G, Smax, D, num_splits, num_cus, ns_out, chunk_out,
                    wgs_for_format(format));
 }
@@ -452,21 +450,25 @@ int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_
                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, float scale,
                                void* out, int32_t out_dtype, float* lse_out, int32_t num_splits,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (kv_dtype == DAS_INT4) return DAS_ENOTSUP;   // INT4 caches are contiguous
-  if (kv_dtype != DAS_BF16 && kv_dtype != DAS_E4M3) return DAS_EINVAL;
-  const bool fp8 = kv_dtype == DAS_E4M3;
-  if (fp8 && (k_scale == nullptr || v_scale == nullptr)) return DAS_EINVAL;
+  if (kv_dtype != DAS_BF16 && kv_dtype != DAS_E4M3 && kv_dtype != DAS_INT4) return DAS_EINVAL;
+  const bool fp8 = kv_dtype == DAS_E4M3, int4 = kv_dtype == DAS_INT4;
+  if ((fp8 || int4) && (k_scale == nullptr || v_scale == nullptr)) return DAS_EINVAL;
+  if (int4 && (((uintptr_t)k_scale & 3u) != 0 || ((uintptr_t)v_scale & 3u) != 0))
+    return DAS_EINVAL;
   if (block_table == nullptr || ((uintptr_t)block_table & 3u) != 0) return DAS_EINVAL;
   if (layout != DAS_PAGED_HND && layout != DAS_PAGED_NHD) return DAS_EINVAL;
   if (max_blocks < 1 || num_pages < 1) return DAS_EINVAL;
   if (page_size < 32 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
     return DAS_ENOTSUP;
   if ((int64_t)max_blocks * page_size > INT32_MAX) return DAS_EINVAL;
-  // one page's rows of one kv-head are addressed with 32-bit byte offsets
-  const int64_t E = fp8 ? 1 : 2;
-  if ((int64_t)page_size * Hkv * D * E > INT32_MAX) return DAS_ENOTSUP;
-  KvCache kv{k_pool, v_pool, fp8 ? k_scale : nullptr, fp8 ? v_scale : nullptr,
-             fp8 ? das::kKvE4m3 : das::kKvBf16};
+  // one page (every kv-head) is addressed with 32-bit byte offsets, and so is
+  // an INT4 page's pool of row scales
+  const int64_t row_bytes = int4 ? D / 2 : (fp8 ? D : 2 * (int64_t)D);
+  if ((int64_t)page_size * Hkv * row_bytes > INT32_MAX) return DAS_ENOTSUP;
+  if (int4 && (int64_t)page_size * Hkv * 4 > INT32_MAX) return DAS_ENOTSUP;
+  KvCache kv{k_pool, v_pool, (fp8 || int4) ? k_scale : nullptr,
+             (fp8 || int4) ? v_scale : nullptr,
+             int4 ? das::kKvInt4 : (fp8 ? das::kKvE4m3 : das::kKvBf16)};
   kv.block_table = block_table;
   kv.max_blocks = max_blocks;
   kv.page_size = page_size;

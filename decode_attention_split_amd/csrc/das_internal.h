@@ -39,7 +39,8 @@ struct SplitArgs {
   const uint16_t* q;         // bf16 [B][Hq][D]
   const void* k;             // [B][Hkv][Smax][D] bf16 or E4M3 codes, [..][D/2] INT4 bytes
   const void* v;
-  const float* k_scale;      // E4M3: fp32 [Hkv]; INT4: fp32 [B][Hkv][Smax]; bf16: unused
+  const float* k_scale;      // E4M3: fp32 [Hkv]; INT4: fp32 [B][Hkv][Smax] (paged: a scale
+                             // pool shaped like the code pool); bf16: unused
   const float* v_scale;
   const int32_t* seq_lens;   // int32 [B]
   int32_t Hq, Hkv, Smax;
@@ -62,6 +63,11 @@ struct SplitArgs {
   int32_t row_stride;        // bytes between rows of one kv-head within a page
   int32_t head_stride;       // bytes between kv-heads within a page
   int64_t page_bytes;        // bytes per page (every kv-head)
+  // Paged INT4 cache: k_scale / v_scale are pools of row scales laid out like
+  // the code pools; strides in floats.
+  int32_t scale_page_stride; // floats per page (every kv-head)
+  int32_t scale_head_stride; // floats between kv-heads within a page
+  int32_t scale_row_stride;  // floats between rows of one kv-head
 };
 
 // Arrival counters live at the start of the workspace, one per (batch row,

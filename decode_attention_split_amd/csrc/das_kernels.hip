@@ -295,13 +295,23 @@ __device__ __forceinline__ void wave_lds_fence() {
 template <int D, int kKv>
 constexpr int kv_row_bytes() { return kKv == kKvInt4 ? D / 2 : (kKv == kKvE4m3 ? D : 2 * D); }
 
-// Static LDS of split_kv_decode<D, G, kKv>: per wave a K tile and either a
-// V tile (G >= 4: p.V on the matrix cores; an INT4 cache adds the tile's row
-// scales) or a p buffer (G <= 2), reused at the end for the wave's state.
+// LDS region of one wave of split_kv_decode<D, G, kKv>: a K tile and either
+// a V tile (G >= 4: p.V on the matrix cores; an INT4 cache adds the tile's
+// row scales) or a p buffer (G <= 2).  At the end of the stream the region
+// holds the wave's state (G >= 4: G rows of D floats), so it is never
+// smaller than that (INT4 tiles with 16 heads are).
+template <int D, int G, int kKv>
+constexpr int wave_region_bytes() {
+  constexpr int tiles = kTile * kv_row_bytes<D, kKv>() * (G >= 4 ? 2 : 1) +
+                        (G >= 4 ? (kKv == kKvInt4 ? 2 * kTile * 4 : 0) : kTile * G * 4);
+  constexpr int state = G >= 4 ? G * D * 4 : 0;
+  return tiles > state ? tiles : state;
+}
+
+// Static LDS of the wave regions of split_kv_decode<D, G, kKv>.
 template <int D, int G, int kKv>
 constexpr int split_smem_bytes() {
-  return kWaves * (kTile * kv_row_bytes<D, kKv>() * (G >= 4 ? 2 : 1) +
-                   (G >= 4 ? (kKv == kKvInt4 ? 2 * kTile * 4 : 0) : kTile * G * 4));
+  return kWaves * wave_region_bytes<D, G, kKv>();
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -344,7 +354,8 @@ constexpr int pow2_floor(int v) { return v < 2 ? v : 2 * pow2_floor(v / 2); }
 // dequantised on chip, right after the load).
 // kPaged: K and V live in page pools listed by a block table (same post,
 // §6); a tile never straddles a page (pages are >= 32 rows, chunks whole
-// pages), so every tile finds its page with one table entry.
+// pages), so every tile finds its page with one table entry.  An INT4 pool
+// comes with pools of row scales laid out like it.
 // ---------------------------------------------------------------------------
 // Waves per SIMD the register allocator must allow.  The INT4 kernels with
 // G = 4 fit four (128 registers, no spills) and are bound by their per-row
@@ -360,7 +371,6 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     void split_kv_decode_kernel(SplitArgs a) {
   constexpr bool kFp8 = kKv == kKvE4m3;
   constexpr bool kInt4 = kKv == kKvInt4;
-  static_assert(!(kInt4 && kPaged), "INT4 caches are contiguous");
   constexpr int kT = kTile;                     // rows per wave per step
   constexpr int kRowBytes = kv_row_bytes<D, kKv>();
   // G >= 4: p.V on the matrix cores, V staged through LDS like K.
@@ -383,7 +393,8 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // scales, one float per row
   constexpr int kScaleBytes = (kMfmaPv && kInt4) ? 2 * kT * 4 : 0;
   constexpr int kPBytes = kMfmaPv ? 0 : kT * G * 4;
-  constexpr int kWaveBytes = kKTileBytes + kVTileBytes + kScaleBytes + kPBytes;
+  constexpr int kWaveBytes = wave_region_bytes<D, G, kKv>();
+  static_assert(kWaveBytes >= kKTileBytes + kVTileBytes + kScaleBytes + kPBytes, "tiles fit");
   constexpr int kSmemBytes = split_smem_bytes<D, G, kKv>();
   constexpr int kKBlocks = D / 32;              // MFMA k-blocks of 32 dims
   constexpr int kNBlocks = D / 16;              // p.V MFMA column blocks of 16 dims
@@ -467,11 +478,13 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + slab, kPaged ? 0 : L * kRowBytes);
   const __amdgpu_buffer_rsrc_t rv_seq =
       make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + slab, kPaged ? 0 : L * kRowBytes);
-  // INT4: the sequence's row scales of K and V, L floats each (rows past the
-  // sequence read as 0, checked per row)
-  const size_t scale_slab = ((size_t)b * a.Hkv + g) * (size_t)a.Smax;
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + (kInt4 ? scale_slab : 0), kInt4 ? L * 4 : 0);
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + (kInt4 ? scale_slab : 0), kInt4 ? L * 4 : 0);
+  // INT4, contiguous cache: the sequence's row scales of K and V, L floats
+  // each (rows past the sequence read as 0, checked per row); a paged cache
+  // builds them per page
+  const size_t scale_slab = kPaged ? 0 : ((size_t)b * a.Hkv + g) * (size_t)a.Smax;
+  const int scale_bytes = (kInt4 && !kPaged) ? L * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(a.k_scale + (kInt4 ? scale_slab : 0), scale_bytes);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(a.v_scale + (kInt4 ? scale_slab : 0), scale_bytes);
   int row_end = 0;                              // end of the chunk being streamed
   const int row_in_load = lane / kLanesPerRow;  // this lane's V row within a load
   const int chunk = lane % kLanesPerRow;        // this lane's 8 elements of a V row
@@ -548,13 +561,24 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
 
   // G <= 2: K straight into the wave's LDS tile, V (and INT4 row scales)
   // into registers.
+  // Paged INT4 cache: the row scales of the page holding rows [p0, p0 +
+  // nvalid) of this kv-head, as bounds-checked buffers (rows past the
+  // sequence read as 0).
+  auto page_scales = [&](int page, int nvalid, __amdgpu_buffer_rsrc_t& sk,
+                         __amdgpu_buffer_rsrc_t& sv) {
+    const size_t so = (size_t)page * (size_t)a.scale_page_stride +
+                      (size_t)g * (size_t)a.scale_head_stride;
+    const int sbytes = ((nvalid - 1) * a.scale_row_stride + 1) * 4;
+    sk = make_rsrc(a.k_scale + so, sbytes);
+    sv = make_rsrc(a.v_scale + so, sbytes);
+  };
+  // INT4: floats between the scales of consecutive rows
+  const int scale_row = kPaged ? a.scale_row_stride : 1;
+
   auto load_tile = [&](int r0, VReg* vr, unsigned char* kbuf, int page) {
-    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
+    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq, sk = rks, sv = rvs;
     int soff = r0 * kRowBytes;
-    if constexpr (kInt4) {
-      row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, (lane % kT) * 4, r0 * 4, 0));
-      row_vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane % kT) * 4, r0 * 4, 0));
-    }
+    int srow = r0;   // INT4: the tile's first row within the scale buffers
     if constexpr (kPaged) {
       // this tile's page; a table entry outside the pool is clamped into it
       // (wrong rows, never an access outside the pool)
@@ -567,6 +591,16 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       rk = make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + off, bytes);
       rv = make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + off, bytes);
       soff = (r0 - p0) * row_stride;
+      if constexpr (kInt4) {
+        page_scales(page, nvalid, sk, sv);
+        srow = r0 - p0;
+      }
+    }
+    if constexpr (kInt4) {
+      row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          sk, (lane % kT) * scale_row * 4, srow * scale_row * 4, 0));
+      row_vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          sv, (lane % kT) * scale_row * 4, srow * scale_row * 4, 0));
     }
 #pragma unroll
     for (int m = 0; m < kKLoads; ++m) {
@@ -601,14 +635,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     float sc;
   };
   auto fetch_tile = [&](int r0, TileRegs& t, int page) {
-    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq;
+    __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq, sk = rks, sv = rvs;
     int soff = r0 * kRowBytes;
-    if constexpr (kInt4) {
-      if (lane < kT)
-        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, lane * 4, r0 * 4, 0));
-      else
-        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (lane - kT) * 4, r0 * 4, 0));
-    }
+    int srow = r0;   // INT4: the tile's first row within the scale buffers
     if constexpr (kPaged) {
       const int slot = r0 >> a.page_shift;
       page = min(max(page, 0), a.num_pages - 1);
@@ -619,6 +648,18 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       rk = make_rsrc(reinterpret_cast<const unsigned char*>(a.k) + off, bytes);
       rv = make_rsrc(reinterpret_cast<const unsigned char*>(a.v) + off, bytes);
       soff = (r0 - p0) * row_stride;
+      if constexpr (kInt4) {
+        page_scales(page, nvalid, sk, sv);
+        srow = r0 - p0;
+      }
+    }
+    if constexpr (kInt4) {
+      if (lane < kT)
+        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            sk, lane * scale_row * 4, srow * scale_row * 4, 0));
+      else
+        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            sv, (lane - kT) * scale_row * 4, srow * scale_row * 4, 0));
     }
 #pragma unroll
     for (int m = 0; m < kKLoads; ++m) {
@@ -1499,9 +1540,7 @@ static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bo
       case 2: return launch_split<128, 2, kKv, kPaged>(B, a, one_per_cu, st);
       case 4: return launch_split<128, 4, kKv, kPaged>(B, a, one_per_cu, st);
       case 8: return launch_split<128, 8, kKv, kPaged>(B, a, one_per_cu, st);
-      case 16:
-        if constexpr (kKv != kKvInt4) return launch_split<128, 16, kKv, kPaged>(B, a, one_per_cu, st);
-        break;
+      case 16: return launch_split<128, 16, kKv, kPaged>(B, a, one_per_cu, st);
     }
   } else if (D == 64) {
     switch (G) {
@@ -1509,9 +1548,7 @@ static hipError_t launch_split_typed(int D, int G, int B, const SplitArgs& a, bo
       case 2: return launch_split<64, 2, kKv, kPaged>(B, a, one_per_cu, st);
       case 4: return launch_split<64, 4, kKv, kPaged>(B, a, one_per_cu, st);
       case 8: return launch_split<64, 8, kKv, kPaged>(B, a, one_per_cu, st);
-      case 16:
-        if constexpr (kKv != kKvInt4) return launch_split<64, 16, kKv, kPaged>(B, a, one_per_cu, st);
-        break;
+      case 16: return launch_split<64, 16, kKv, kPaged>(B, a, one_per_cu, st);
     }
   }
   return hipErrorInvalidValue;
@@ -1527,8 +1564,8 @@ hipError_t launch_split_kv_decode(int D, int G, int kv_format, bool paged, int B
       return paged ? launch_split_typed<kKvE4m3, true>(D, G, B, a, one_per_cu, st)
                    : launch_split_typed<kKvE4m3, false>(D, G, B, a, one_per_cu, st);
     case kKvInt4:
-      if (paged) return hipErrorInvalidValue;
-      return launch_split_typed<kKvInt4, false>(D, G, B, a, one_per_cu, st);
+      return paged ? launch_split_typed<kKvInt4, true>(D, G, B, a, one_per_cu, st)
+                   : launch_split_typed<kKvInt4, false>(D, G, B, a, one_per_cu, st);
   }
   return hipErrorInvalidValue;
 }

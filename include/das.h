@@ -46,8 +46,8 @@
  *     stream-ordered; the call returns without waiting for the GPU.
  *   - Calls are re-entrant.  Concurrent calls must not share a workspace.
  *   - Supported shapes: head dim D in {64, 128}; GQA group G = Hq / Hkv in
- *     {1, 2, 4, 8, 16} (Hq a multiple of Hkv; 16 with bf16 and E4M3 caches,
- *     DAS_ENOTSUP with INT4); 1 <= B <= 65535; 1 <= Hkv <= 65535;
+ *     {1, 2, 4, 8, 16} (Hq a multiple of Hkv) with every cache format;
+ *     1 <= B <= 65535; 1 <= Hkv <= 65535;
  *     1 <= Smax with (Smax + 256) * D * 2 < 2^31 (one sequence's K rows are
  *     addressed with 32-bit byte offsets); num_splits <= DAS_MAX_SPLITS.
  *   - Query head h reads kv-head h / G.
@@ -242,8 +242,8 @@ int das_split_kv_decode_fp8(const void* q, const void* k_cache, const void* v_ca
  * The codes become exact bf16 integers on chip; a row's K scale multiplies its
  * finished dot product and its V scale its softmax weight.  A sequence's rows
  * are addressed with 32-bit byte offsets: (Smax + 256) * D / 2 < 2^31.  NULL
- * or misaligned k_scale or v_scale: DAS_EINVAL.  There is no paged INT4 cache
- * (das_decode_attention_paged returns DAS_ENOTSUP for DAS_INT4).
+ * or misaligned k_scale or v_scale: DAS_EINVAL.  A paged INT4 cache: see
+ * das_decode_attention_paged.
  */
 int das_decode_attention_int4(const void* q, const void* k_cache, const void* v_cache,
                               const float* k_scale, const float* v_scale, const int32_t* seq_lens,
@@ -267,22 +267,26 @@ int das_split_kv_decode_int4(const void* q, const void* k_cache, const void* v_c
  * row j % page_size of page block_table[b][j / page_size]:
  *   k_pool, v_pool  [num_pages][Hkv][page_size][D] (DAS_PAGED_HND) or
  *                   [num_pages][page_size][Hkv][D] (DAS_PAGED_NHD), elements
- *                   of kv_dtype: DAS_BF16, or DAS_E4M3 with k_scale/v_scale
- *                   as in das_decode_attention_fp8 (ignored for DAS_BF16);
- *                   DAS_INT4: DAS_ENOTSUP
+ *                   of kv_dtype: DAS_BF16; DAS_E4M3 with k_scale/v_scale
+ *                   as in das_decode_attention_fp8; or DAS_INT4, codes as in
+ *                   das_decode_attention_int4 (a row is D/2 bytes), with
+ *                   k_scale/v_scale pools of fp32 row scales laid out like the
+ *                   code pools: [num_pages][Hkv][page_size] (HND) or
+ *                   [num_pages][page_size][Hkv] (NHD), 4-byte aligned
+ *                   (k_scale/v_scale are ignored for DAS_BF16)
  *   block_table     device int32 [B][max_blocks]; entries of pages a sequence
  *                   does not reach are never read; an entry outside
  *                   [0, num_pages) is clamped into it on the device (wrong
  *                   rows, never an access outside the pool)
  *   page_size       a power of two, 32 ... 65536 rows (DAS_ENOTSUP otherwise)
  *   seq_lens[b]     device int32, clamped to [0, max_blocks * page_size]
- * Splits cover whole pages: the plan is das_plan's for Smax = max_blocks *
- * page_size with the chunk rounded up to a multiple of page_size, so a
+ * Splits cover whole pages: the plan is das_plan_kv's for kv_dtype and Smax =
+ * max_blocks * page_size with the chunk rounded up to a multiple of page_size, so a
  * workspace of das_decode_workspace_bytes(B, Hq, Hkv, max_blocks *
  * page_size, D, num_splits, 0) bytes always suffices.  q, out, lse_out,
  * num_splits, the workspace precondition, stream, errors: as for
- * das_decode_attention.  One page's rows of one kv-head are addressed with
- * 32-bit offsets: page_size * Hkv * D * element bytes < 2^31.
+ * das_decode_attention.  One page is addressed with 32-bit offsets:
+ * page_size * Hkv * (bytes of a row of D elements) < 2^31.
  */
 int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_pool,
                                int32_t kv_dtype, const float* k_scale, const float* v_scale,

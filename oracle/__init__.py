@@ -24,7 +24,7 @@ Pieces:
   integer K/V cache (same post, §4, which names INT4 beside FP8), read as
   two's-complement codes, two per byte (element 2i in the low nibble), with
   one fp32 scale per cached row (batch row, kv-head, token) for K and for V.
-* ``gather_paged`` / ``attention_paged`` -- a paged K/V cache (FlashDecoding++
+* ``gather_paged`` / ``gather_paged_int4`` / ``attention_paged`` -- a paged K/V cache (FlashDecoding++
   post, §6: engines keep K/V in blocks allocated anywhere in a pool, listed
   per sequence by a block table, and map each block onto a slice of a
   chunk).  Row j of sequence b is row j mod P of block
@@ -321,6 +321,21 @@ def attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, la
     k = gather_paged(k_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
     v = gather_paged(v_pool, block_table, seq_lens, page_size, layout, smax, 0x7FC0)
     return (lib or default()).attention(q, k, v, seq_lens, scale)
+
+
+def gather_paged_int4(paged):
+    """Contiguous INT4 codes and row scales of a paged INT4 cache (a
+    workloads.PagedInputs with scale pools): codes [B][Hkv][smax][D/2] (0x88
+    past each sequence) and scales [B][Hkv][smax] (NaN past each sequence),
+    gathered like ``gather_paged``."""
+    smax = int(np.asarray(paged.block_table).shape[1]) * paged.page_size
+    sl = paged.base.seq_lens
+    args = (paged.block_table, sl, paged.page_size, paged.layout, smax)
+    k = gather_paged(paged.k_pool, *args, 0x88)
+    v = gather_paged(paged.v_pool, *args, 0x88)
+    ks = gather_paged(paged.k_scale_pool[..., None], *args, np.float32(np.nan))[..., 0]
+    vs = gather_paged(paged.v_scale_pool[..., None], *args, np.float32(np.nan))[..., 0]
+    return k, v, ks, vs
 
 
 def abs_attention_paged(q, k_pool, v_pool, block_table, seq_lens, page_size: int, layout: int,

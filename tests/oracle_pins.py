@@ -540,6 +540,27 @@ def pin_paged_attention_equals_contiguous(lib):
     assert np.array_equal(o, ro) and np.array_equal(l, rl)
 
 
+def pin_paged_int4_gather_inverts_the_generators_scatter(lib):
+    """INT4 page pools and their row-scale pools: the gather returns exactly
+    the contiguous codes and scales the generator drew (both layouts), 0x88
+    and NaN past each sequence, and attention over them is bitwise the
+    contiguous INT4 definition."""
+    cfg = workloads.custom_config(3, 8, 2, 32, 150)
+    for layout in (oracle.PAGED_HND, oracle.PAGED_NHD):
+        x = workloads.make_paged_inputs(cfg, 43 + layout, 32, layout, seq_lens=(150, 33, 0),
+                                        int4=True)
+        k, v, ks, vs = oracle.gather_paged_int4(x)
+        b = x.base
+        for i, L in enumerate(b.seq_lens):
+            assert np.array_equal(k[i, :, :L], b.k[i, :, :L]) and np.array_equal(v[i, :, :L], b.v[i, :, :L])
+            assert np.array_equal(ks[i, :, :L], b.k_scale[i, :, :L])
+            assert np.array_equal(vs[i, :, :L], b.v_scale[i, :, :L])
+            assert np.all(k[i, :, L:] == 0x88) and np.all(np.isnan(vs[i, :, L:]))
+        o, l = lib.attention_int4(b.q, k, v, ks, vs, b.seq_lens, b.scale)
+        ro, rl = lib.attention_int4(b.q, b.k, b.v, b.k_scale, b.v_scale, b.seq_lens, b.scale)
+        assert np.array_equal(o, ro) and np.array_equal(l, rl)
+
+
 # ---- magnitude form: sum_j w_j |v_j| / Z (the scale of the bf16-output bound) ----
 
 def pin_abs_zero_query_gives_mean_magnitude(lib):

@@ -18,7 +18,7 @@ from gpu_helpers import check_bf16, check_f32, dev, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8)]
+SHAPES = [(D, G) for D in (64, 128) for G in (1, 2, 4, 8, 16)]
 
 
 def upload_int4(x: workloads.Int4Inputs):
@@ -68,7 +68,7 @@ def test_int4_small_shapes_all_split_counts(D, G):
         check_f32(out, lse, *ref, f"int4 D={D} G={G} ns={ns}")
 
 
-@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (64, 4)],
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 1), (128, 2), (64, 4), (128, 16)],
                          ids=lambda v: str(v))
 def test_int4_edge_lengths(D, G):
     lens = (0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300)
@@ -103,7 +103,7 @@ def test_int4_extreme_codes_and_scales():
         check_f32(out, lse, *ref, f"int4 extreme codes ns={ns}")
 
 
-@pytest.mark.parametrize("D,G", [(128, 4), (64, 1), (128, 8)], ids=lambda v: str(v))
+@pytest.mark.parametrize("D,G", [(128, 4), (64, 1), (128, 8), (64, 16)], ids=lambda v: str(v))
 def test_int4_bf16_output(D, G):
     cfg = workloads.custom_config(3, 4 * G, 4, D, 2000, k_mult=4.0)
     x = workloads.make_int4_inputs(cfg, 8300 + D + G, seq_lens=(2000, 1, 1234))
@@ -161,11 +161,17 @@ def test_int4_named_config_full_size(idx):
     torch.cuda.empty_cache()
 
 
-def test_int4_group_of_16_is_not_supported():
-    """A wave's end-of-stream state for 16 heads does not fit in an INT4 tile
-    region: the call is refused before anything is launched."""
-    cfg = workloads.custom_config(1, 32, 2, 128, 256)
-    x = workloads.make_int4_inputs(cfg, 8500, seq_lens=(256,))
-    with pytest.raises(das.DasError) as e:
-        run_int4(x, 0)
-    assert e.value.status == das.DAS_ENOTSUP
+def test_int4_group_of_16_at_a_405b_shape():
+    """GQA groups of 16 heads (Hq=128, Hkv=8, D=128, a Llama-3.1-405B-shaped
+    decode) over a 32K-token INT4 cache at full size: the wave state of 16
+    heads fills a wave's LDS region of its own.  Automatic plan and one split
+    against the oracle over every output."""
+    cfg = workloads.custom_config(1, 128, 8, 128, 32768)
+    note("case int4 G=16 405B-shaped: generating inputs")
+    x = workloads.make_int4_inputs(cfg, 8500, seq_lens=(32768,))
+    ref = ref_int4(x)
+    t = upload_int4(x)
+    for ns in (0, 1):
+        note(f"case int4 G=16 405B-shaped: num_splits={ns}")
+        out, lse = run_int4(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"int4 G=16 ns={ns}")

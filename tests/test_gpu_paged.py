@@ -1,6 +1,7 @@
 """Paged K/V cache (FlashDecoding++ post, §6): das_decode_attention_paged vs the
 fp64 oracle over the gathered rows, element by element, on seeded inputs
-scattered into shuffled page pools with spare NaN pages.  Same tolerances as
+scattered into shuffled page pools with spare NaN pages (bf16, E4M3 and INT4
+pools; INT4 with row-scale pools laid out like the code pools).  Same tolerances as
 the contiguous cache (fp32 output max|err| <= 5e-4, LSE max|err| <= 1e-4)."""
 import numpy as np
 import pytest
@@ -21,6 +22,9 @@ def upload_paged(x: workloads.PagedInputs):
     if x.k_pool.dtype == np.uint16:
         kp, vp = to_dev(x.k_pool), to_dev(x.v_pool)
         ks = vs = None
+    elif x.k_scale_pool is not None:      # INT4: row-scale pools
+        kp, vp = torch.from_numpy(x.k_pool).to(d), torch.from_numpy(x.v_pool).to(d)
+        ks, vs = torch.from_numpy(x.k_scale_pool).to(d), torch.from_numpy(x.v_scale_pool).to(d)
     else:
         kp, vp = torch.from_numpy(x.k_pool).to(d), torch.from_numpy(x.v_pool).to(d)
         ks, vs = torch.from_numpy(x.base.k_scale).to(d), torch.from_numpy(x.base.v_scale).to(d)
@@ -30,14 +34,18 @@ def upload_paged(x: workloads.PagedInputs):
 
 def run_paged(x, num_splits=0, out_dtype=torch.float32, tensors=None):
     q, kp, vp, bt, sl, ks, vs = tensors if tensors is not None else upload_paged(x)
-    out, lse = das.das_decode_attention_paged(q, kp, vp, bt, sl, x.base.scale, x.page_size,
-                                              x.layout, k_scale=ks, v_scale=vs,
-                                              out_dtype=out_dtype, num_splits=num_splits)
+    out, lse = das.das_decode_attention_paged(
+        q, kp, vp, bt, sl, x.base.scale, x.page_size, x.layout, k_scale=ks, v_scale=vs,
+        out_dtype=out_dtype, num_splits=num_splits,
+        kv_dtype=das.DAS_INT4 if x.k_scale_pool is not None else None)
     torch.cuda.synchronize()
     return out, lse
 
 
 def ref_paged(x):
+    if x.k_scale_pool is not None:
+        k, v, ks, vs = oracle.gather_paged_int4(x)
+        return oracle.attention_int4(x.base.q, k, v, ks, vs, x.base.seq_lens, x.base.scale)
     if x.k_pool.dtype == np.uint16:
         return oracle.attention_paged(x.base.q, x.k_pool, x.v_pool, x.block_table,
                                       x.base.seq_lens, x.page_size, x.layout, x.base.scale)
@@ -102,6 +110,58 @@ def test_paged_fp8(layout):
         note(f"case paged fp8 layout={layout} num_splits={ns}")
         out, lse = run_paged(x, ns, tensors=t)
         check_f32(out, lse, *ref, f"paged fp8 L{layout} ns={ns}")
+
+
+@pytest.mark.parametrize("layout", [HND, NHD], ids=["HND", "NHD"])
+@pytest.mark.parametrize("D,G", [(D, G) for D in (64, 128) for G in (1, 2, 4, 8, 16)],
+                         ids=lambda v: str(v))
+def test_paged_int4(D, G, layout):
+    """INT4 page pools with row-scale pools laid out like them: every (D, G),
+    both layouts, two page sizes, several split counts."""
+    cfg = workloads.custom_config(3, 2 * G, 2, D, 1000, k_mult=2.0)
+    for P in (32, 256):
+        x = workloads.make_paged_inputs(cfg, 8600 + 10 * D + G + P, P, layout,
+                                        seq_lens=(1000, 777, 33), int4=True)
+        ref = ref_paged(x)
+        t = upload_paged(x)
+        for ns in (0, 1, 3, 7):
+            note(f"case paged int4 D={D} G={G} P={P} layout={layout} num_splits={ns}")
+            out, lse = run_paged(x, ns, tensors=t)
+            check_f32(out, lse, *ref, f"paged int4 D={D} G={G} P={P} L{layout} ns={ns}")
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_paged_int4_edge_lengths(P):
+    """INT4 pools: partial last pages, a page boundary either side, L = 0, 1."""
+    lens = (0, 1, P - 1, P, P + 1, 2 * P - 1, 2 * P, 2 * P + 1, 5 * P + 3)
+    cfg = workloads.custom_config(len(lens), 8, 2, 128, 5 * P + 3)
+    x = workloads.make_paged_inputs(cfg, 8700 + P, P, NHD, seq_lens=lens, int4=True)
+    ref = ref_paged(x)
+    t = upload_paged(x)
+    for ns in (0, 1, 2, 5):
+        note(f"case paged int4 edge lengths P={P} num_splits={ns}")
+        out, lse = run_paged(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"paged int4 edge P={P} ns={ns}")
+        assert torch.all(out[0] == 0) and torch.all(lse[0] == -float("inf"))
+
+
+@pytest.mark.parametrize("idx,P,layout", [(1, 64, HND), (3, 256, NHD)],
+                         ids=["gqa_32k_P64_HND", "varlen_b64_P256_NHD"])
+def test_paged_int4_named_config_full_size(idx, P, layout):
+    """Named configs at full size in INT4 page pools, automatic plan, against
+    the oracle over every output."""
+    cfg = workloads.CONFIGS[idx]
+    note(f"case paged int4 full config {cfg.name} P={P}: generating inputs")
+    x = workloads.make_paged_inputs(cfg, 42 + idx, P, layout, int4=True)
+    t = upload_paged(x)
+    note(f"case paged int4 full config {cfg.name}: auto splits")
+    out, lse = run_paged(x, 0, tensors=t)
+    note(f"case paged int4 full config {cfg.name}: oracle on all {len(x.base.seq_lens)} rows")
+    b = x.base
+    ref_o, ref_l = oracle.attention_int4(b.q, b.k, b.v, b.k_scale, b.v_scale, b.seq_lens, b.scale)
+    check_f32(out, lse, ref_o, ref_l, f"paged int4 {cfg.name}")
+    del t
+    torch.cuda.empty_cache()
 
 
 def test_paged_table_entries_outside_the_pool_are_contained():

@@ -2,8 +2,8 @@
 oracle: head dims, group sizes, kv-head counts, batch sizes, cache lengths
 (log-uniform up to 20000 rows), sequence lengths (empty, tile and page
 edges, full), forced and automatic split counts, softmax scales, fp32 and
-bf16 outputs, and every cache format (bf16, E4M3, INT4, bf16 and E4M3 page
-pools in both layouts).  Each case is drawn from its own seed, so a failing
+bf16 outputs, and every cache format (bf16, E4M3, INT4, and bf16, E4M3 and
+INT4 page pools in both layouts).  Each case is drawn from its own seed, so a failing
 case is named by that seed.
 
 Every case runs with fp32 output against the oracle (max|err| <= 5e-4 on
@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 GROUPS = 16           # test functions
 CASES_PER_GROUP = 32  # cases per test function
-FORMATS = ("bf16", "fp8", "int4", "paged", "paged_fp8")
+FORMATS = ("bf16", "fp8", "int4", "paged", "paged_fp8", "paged_int4")
 
 
 def draw_case(seed: int) -> dict:
@@ -35,8 +35,6 @@ def draw_case(seed: int) -> dict:
     Hkv = int(rng.integers(1, 5))
     B = int(rng.integers(1, 9))
     fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
-    if fmt == "int4" and G == 16:
-        G = 8     # INT4 caches support groups of up to 8 heads
     smax = int(np.exp(rng.uniform(0.0, np.log(20000.0))))   # log-uniform, 1 .. 20000
     page = int(rng.choice([32, 64, 128, 256])) if fmt.startswith("paged") else 0
     # lengths: uniform, plus edge values around 32-row tiles and pages
@@ -95,6 +93,22 @@ def run_case(c: dict, out_dtype, want_mag: bool = False):
             to_dev(x.q), torch.from_numpy(x.k).to(d), torch.from_numpy(x.v).to(d),
             torch.from_numpy(x.k_scale).to(d), torch.from_numpy(x.v_scale).to(d),
             torch.from_numpy(x.seq_lens).to(d), x.scale, out_dtype=out_dtype, num_splits=ns)
+    elif fmt == "paged_int4":
+        x = workloads.make_paged_inputs(cfg, c["seed"], c["page"], c["layout"], seq_lens=lens,
+                                        int4=True)
+        x.base.scale = c["scale"]
+        k, v, ks, vs = oracle.gather_paged_int4(x)
+        b = x.base
+        ref = oracle.attention_int4(b.q, k, v, ks, vs, b.seq_lens, b.scale)
+        mag = (lambda: oracle.abs_attention_int4(b.q, k, v, ks, vs, b.seq_lens, b.scale)
+               + 8.0 * oracle.abs_attention_int4(b.q, k, np.full_like(v, 0x11), ks, vs,
+                                                 b.seq_lens, b.scale))
+        out, lse = das.das_decode_attention_paged(
+            to_dev(b.q), torch.from_numpy(x.k_pool).to(d), torch.from_numpy(x.v_pool).to(d),
+            torch.from_numpy(x.block_table).to(d), torch.from_numpy(b.seq_lens).to(d), b.scale,
+            x.page_size, x.layout, k_scale=torch.from_numpy(x.k_scale_pool).to(d),
+            v_scale=torch.from_numpy(x.v_scale_pool).to(d), out_dtype=out_dtype,
+            num_splits=ns, kv_dtype=das.DAS_INT4)
     else:
         fp8 = fmt == "paged_fp8"
         x = workloads.make_paged_inputs(cfg, c["seed"], c["page"], c["layout"], seq_lens=lens,

@@ -221,8 +221,17 @@ def test_int4_row_bound_is_four_times_the_bf16_one(lib):
     assert _call_decode_int4(lib, Smax=smax, ws=0) == das.DAS_EWORKSPACE
 
 
-def test_paged_int4_is_not_supported(lib):
-    assert _call_paged(lib, kvt=das.DAS_INT4, ks=16, vs=16) == das.DAS_ENOTSUP
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0), das.DAS_EINVAL), (dict(vs=0), das.DAS_EINVAL),       # INT4 needs scale pools
+    (dict(ks=18), das.DAS_EINVAL), (dict(vs=2), das.DAS_EINVAL),      # misaligned scale pools
+    (dict(ws=0), das.DAS_EWORKSPACE),                                 # checks pass up to here
+])
+def test_paged_int4_argument_checks(lib, kw, status):
+    """A paged INT4 cache takes row-scale pools: missing or misaligned ones
+    are refused before anything is launched (fake pointers)."""
+    a = dict(kvt=das.DAS_INT4, ks=16, vs=16)
+    a.update(kw)
+    assert _call_paged(lib, **a) == status
 
 
 def test_merge_argument_checks(lib):
@@ -293,15 +302,14 @@ def test_paged_argument_checks(lib, kw, status):
     assert _call_paged(lib, **kw) == status
 
 
-def test_group_of_16_plans_and_int4_refuses_it():
-    # G = 16 (e.g. Hq = 128, Hkv = 8): bf16 and E4M3 caches plan as usual with
-    # chunks of at least 1024 rows; an INT4 cache does not support it
+def test_group_of_16_plans_for_every_cache_format():
+    # G = 16 (e.g. Hq = 128, Hkv = 8): every cache format plans with chunks of
+    # at least 1024 rows; bf16 and E4M3 share the plan, INT4 aims for every CU
     ns, chunk = plan(1, 8, 16, 32768, 128)
     assert chunk >= 1024 and (ns - 1) * chunk < 32768 <= ns * chunk
     assert das.das_plan_kv(das.DAS_E4M3, 1, 8, 16, 32768, 128, 0, 256) == (ns, chunk)
-    with pytest.raises(das.DasError) as e:
-        das.das_plan_kv(das.DAS_INT4, 1, 8, 16, 32768, 128, 0, 256)
-    assert e.value.status == das.DAS_ENOTSUP
+    ns4, chunk4 = das.das_plan_kv(das.DAS_INT4, 1, 8, 16, 32768, 128, 0, 256)
+    assert chunk4 >= 1024 and (ns4 - 1) * chunk4 < 32768 <= ns4 * chunk4 and ns4 >= ns
     with pytest.raises(das.DasError) as e:
         das.das_plan(1, 8, 32, 32768, 128, 0, 256)          # G = 32
     assert e.value.status == das.DAS_ENOTSUP

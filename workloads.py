@@ -23,11 +23,13 @@ Recipe (one config = one seed, ``seed = 42 + config index``):
   (0x7FC0) so that any kernel reading them contaminates its result.
 * ``scale = 1/sqrt(D)`` rounded to float32 (the library takes a float).
 
-Paged caches (``make_paged_inputs``): the contiguous bf16 draw above, then
-every sequence's rows are cut into pages of P rows and the pages are placed
-in a pool in an order given by ``PCG64(seed + 7919).permutation``; the pool
-also holds a few spare pages (all NaN) that no table points to, and the
-block-table entries past a sequence's last page point to a spare page.
+Paged caches (``make_paged_inputs``): the contiguous draw above (bf16, E4M3
+or INT4), then every sequence's rows are cut into pages of P rows and the
+pages are placed in a pool in an order given by
+``PCG64(seed + 7919).permutation``; the pool also holds a few spare pages
+(all NaN, or INT4 code byte 0x88) that no table points to, and the
+block-table entries past a sequence's last page point to a spare page.  An
+INT4 cache's row scales are scattered the same way into scale pools.
 
 8-bit (E4M3) K/V caches (``make_fp8_inputs``): q as above; per kv-head
 scales ``k_scale[g] = k_mult * (4 + g) / 64`` and ``v_scale[g] = (3 + g) / 64``
@@ -419,12 +421,14 @@ def scatter_to_pages(k: np.ndarray, v: np.ndarray, seq_lens: np.ndarray, page_si
 
 @dataclasses.dataclass
 class PagedInputs:
-    base: object              # Inputs or Fp8Inputs: the same rows as a contiguous cache
+    base: object              # Inputs, Fp8Inputs or Int4Inputs: the same rows, contiguous
     page_size: int
     layout: int
     k_pool: np.ndarray        # [num_pages][Hkv][P][D] (HND) or [num_pages][P][Hkv][D] (NHD)
-    v_pool: np.ndarray
+    v_pool: np.ndarray        # (INT4: D/2 bytes of codes per row)
     block_table: np.ndarray   # int32 [B][max_blocks]
+    k_scale_pool: Optional[np.ndarray] = None   # INT4: float32 [num_pages][Hkv][P] (HND)
+    v_scale_pool: Optional[np.ndarray] = None   # or [num_pages][P][Hkv] (NHD)
 
     @property
     def kv_bytes(self) -> int:
@@ -433,10 +437,17 @@ class PagedInputs:
 
 def make_paged_inputs(cfg: Config, seed: int, page_size: int, layout: int = PAGED_HND,
                       smax: Optional[int] = None, seq_lens: Optional[Sequence[int]] = None,
-                      spare_pages: int = 3, fp8: bool = False) -> PagedInputs:
-    """``make_inputs`` (or ``make_fp8_inputs``; same seed, same rows), scattered
-    into a page pool."""
-    if fp8:
+                      spare_pages: int = 3, fp8: bool = False, int4: bool = False) -> PagedInputs:
+    """``make_inputs`` (or ``make_fp8_inputs`` / ``make_int4_inputs``; same
+    seed, same rows), scattered into a page pool.  An INT4 cache's row scales
+    go into scale pools laid out like the code pools (same pages, same
+    table); spare rows hold code byte 0x88 and a NaN scale."""
+    if fp8 and int4:
+        raise ValueError("one cache format at a time")
+    if int4:
+        base = make_int4_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        fill = np.uint8(0x88)
+    elif fp8:
         base = make_fp8_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
         fill = E4M3_NAN
     else:
@@ -444,4 +455,11 @@ def make_paged_inputs(cfg: Config, seed: int, page_size: int, layout: int = PAGE
         fill = BF16_QNAN
     k_pool, v_pool, table = scatter_to_pages(base.k, base.v, base.seq_lens, page_size, layout,
                                              seed, fill, spare_pages)
-    return PagedInputs(base, int(page_size), layout, k_pool, v_pool, table)
+    ks_pool = vs_pool = None
+    if int4:
+        ks_pool, vs_pool, table_s = scatter_to_pages(
+            base.k_scale[..., None], base.v_scale[..., None], base.seq_lens, page_size, layout,
+            seed, np.float32(np.nan), spare_pages)
+        assert np.array_equal(table, table_s)
+        ks_pool, vs_pool = ks_pool[..., 0].copy(), vs_pool[..., 0].copy()
+    return PagedInputs(base, int(page_size), layout, k_pool, v_pool, table, ks_pool, vs_pool)
