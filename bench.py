@@ -408,7 +408,8 @@ class Workload:
         us = self.event_us(self.calls(splits, out, lse), n, warmup)
         ns, chunk = self.plan(splits)
         gbs = self.kv_bytes / (us * 1e-6) / 1e9
-        return {"workload": self.cfg.name, "splits": "auto" if splits == 0 else splits,
+        return {"workload": self.cfg.name, "G": self.Hq // self.Hkv,
+                "splits": "auto" if splits == 0 else splits,
                 "plan": f"{ns} x {chunk}", "merge": fused_merge(self.B, self.Hkv, ns, self.cus),
                 "out_dtype": out_dtype, "kv_bytes": self.kv_bytes, "us_per_call": round(us, 2),
                 "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "launches": n}
@@ -424,13 +425,18 @@ def per_config_table(args, headline: "Workload") -> list:
     import workloads
 
     rows = []
-    for idx in range(len(workloads.CONFIGS)):
+    # the named configs, then the 32K-token cache of config 1 with other
+    # GQA groups: Hq = 8 and 16 (G = 1, 2: the vector-ALU path at long
+    # context, the per-head grid of [FD++] §2) and Hq = 128 (G = 16)
+    jobs = [(idx, 0) for idx in range(len(workloads.CONFIGS))] + [(1, 8), (1, 16), (1, 128)]
+    for idx, hq in jobs:
         if headline is not None and idx == args.config and headline.kv_dtype == "bf16" \
-                and headline.paged is None and not args.hq:
+                and headline.paged is None and hq == args.hq:
             w = headline
         else:
-            w = Workload(args, idx)
-        for splits, out_dtype in ((0, "f32"), (0, "bf16"), (1, "f32")):
+            w = Workload(args, idx, hq=hq)
+        variants = ((0, "f32"), (0, "bf16"), (1, "f32")) if not hq else ((0, "f32"),)
+        for splits, out_dtype in variants:
             rows.append(w.row(splits, out_dtype, args.table_steps, args.table_warmup))
         print(f"bench: table {w.cfg.name} done", file=sys.stderr, flush=True)
         if w is not headline:

@@ -1312,106 +1312,86 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2: lse_combine.  Grid (Hq, B), 256 threads.
+// Phase 2: lse_combine.  One wave per (batch row, query head): 4 waves per
+// workgroup, 256 threads.
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
+constexpr int kCombineRows = kCombineThreads / 64;   // (b, h) rows per workgroup
 
-// One workgroup per (query head, batch row).  Thread t owns the float4 quad
-// t % (D/4) of the output row and the splits t / (D/4) + k * groups.  Each
-// thread loads the statistics and partial rows of its first kRegSplits
-// splits together, so a plan with up to groups * kRegSplits splits needs a
-// single round trip to memory; larger plans loop.
-constexpr int kRegSplits = 8;
-
-// max or sum over the workgroup; every thread gets the result
-template <bool kMax>
-__device__ __forceinline__ float block_reduce2(float v, float* red) {
-  auto op = [](float u, float w) { return kMax ? fmaxf(u, w) : u + w; };
-  v = row_reduce16<kMax>(v);
-  v = op(op(lane_value(v, 0), lane_value(v, 16)), op(lane_value(v, 32), lane_value(v, 48)));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombineThreads / 64; ++w) r = op(r, red[w]);
-  __syncthreads();
-  return r;
-}
+// Each lane owns the float4 quad lane % (D/4) of the output row; the wave's
+// 64 / (D/4) lane groups take the splits grp, grp + groups, ... and merge
+// them online, loading kCombineBatch splits per round trip (statistics and
+// partial rows together).  The groups then combine with row swaps (global
+// max, rescale, sum), in a fixed order: no LDS and no barrier.
+constexpr int kCombineBatch = 4;
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a, int rows) {
   constexpr int kQuads = D / 4;
-  constexpr int kGroups = kCombineThreads / kQuads;
-  __shared__ float red[kCombineThreads / 64];
-  __shared__ float4 part[kGroups][kQuads];
-
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int quad = tid % kQuads, grp = tid / kQuads;
+  constexpr int kGroups = 64 / kQuads;                 // 2 (D = 128) or 4 (D = 64)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kCombineRows + (threadIdx.x >> 6);   // b * Hq + h
+  if (row >= rows) return;
+  const int b = row / a.Hq;
+  const int quad = lane % kQuads, grp = lane / kQuads;
   const int L = clamp_len(a.seq_lens[b], a.Smax);
   const int nsb = min(a.ns, (L + a.chunk - 1) / a.chunk);  // splits this sequence used
-  const size_t qh = (size_t)b * a.Hq + h;
+  const size_t qh = (size_t)row;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml + qh * a.ns * 2);
   const float4* po = reinterpret_cast<const float4*>(a.ws_o + qh * a.ns * D) + quad;
 
-  // one round trip: statistics and partial rows of this thread's first splits
-  float2 st[kRegSplits];
-  float4 pr[kRegSplits];
-#pragma unroll
-  for (int u = 0; u < kRegSplits; ++u) {
-    const int c = grp + u * kGroups;
-    if (c < nsb) {
-      st[u] = ml[c];
-      pr[u] = po[(size_t)c * kQuads];
-    } else {
-      st[u] = make_float2(-INFINITY, 0.f);
-      pr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < kRegSplits; ++u) mx = fmaxf(mx, st[u].x);
-  for (int c = grp + kRegSplits * kGroups; c < nsb; c += kGroups) mx = fmaxf(mx, ml[c].x);
-  const float M = block_reduce2<true>(mx, red);
-
+  float mt = -INFINITY, ls = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float ls = 0.f;
-  if (nsb > 0) {
+  for (int c0 = grp; c0 < nsb; c0 += kCombineBatch * kGroups) {
+    float2 st[kCombineBatch];
+    float4 pr[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < kRegSplits; ++u) {
-      const float w = fast_exp2(st[u].x - M);  // exp2(-inf) = 0 for unused slots
-      o.x = fmaf(w, pr[u].x, o.x);
-      o.y = fmaf(w, pr[u].y, o.y);
-      o.z = fmaf(w, pr[u].z, o.z);
-      o.w = fmaf(w, pr[u].w, o.w);
-      ls = fmaf(w, st[u].y, ls);
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int c = c0 + k * kGroups;
+      st[k] = c < nsb ? ml[c] : make_float2(-INFINITY, 0.f);
+      pr[k] = c < nsb ? po[(size_t)c * kQuads] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int c = grp + kRegSplits * kGroups; c < nsb; c += kGroups) {
-      const float2 sc = ml[c];
-      const float4 u4 = po[(size_t)c * kQuads];
-      const float w = fast_exp2(sc.x - M);
-      o.x = fmaf(w, u4.x, o.x);
-      o.y = fmaf(w, u4.y, o.y);
-      o.z = fmaf(w, u4.z, o.z);
-      o.w = fmaf(w, u4.w, o.w);
-      ls = fmaf(w, sc.y, ls);
+    float bm = st[0].x;   // finite: split c0 < nsb is in the batch
+#pragma unroll
+    for (int k = 1; k < kCombineBatch; ++k) bm = fmaxf(bm, st[k].x);
+    const float mn = fmaxf(mt, bm);
+    const float alpha = fast_exp2(mt - mn);   // 0 on the first batch
+    o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
+    ls *= alpha;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const float w = fast_exp2(st[k].x - mn);   // 0 for the padding slots
+      o.x = fmaf(w, pr[k].x, o.x);
+      o.y = fmaf(w, pr[k].y, o.y);
+      o.z = fmaf(w, pr[k].z, o.z);
+      o.w = fmaf(w, pr[k].w, o.w);
+      ls = fmaf(w, st[k].y, ls);
     }
+    mt = mn;
   }
-  // every quad of a group saw the same splits: count each split's sum once
-  const float lsum = block_reduce2<false>(quad == 0 ? ls : 0.f, red);
-  part[grp][quad] = o;
-  __syncthreads();
-  if (tid < D) {
-    const float* pf = reinterpret_cast<const float*>(&part[0][0]);
-    float t = 0.f;
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) t += pf[gi * D + tid];
-    const float val = (nsb == 0) ? 0.f : t / lsum;
-    if (a.out_bf16)
-      reinterpret_cast<uint16_t*>(a.out)[qh * D + tid] = f32_to_bf16_rne(val);
-    else
-      reinterpret_cast<float*>(a.out)[qh * D + tid] = val;
-    if (tid == 0 && a.lse != nullptr)
-      a.lse[qh] = (nsb == 0) ? -INFINITY : (M + __log2f(lsum)) * kLn2;
+  // combine the groups (a group without splits has max -inf and weighs 0)
+  constexpr int kGroupBit = log2_int(kQuads);
+  const float M = reduce_lane_bits<kGroupBit, true>(mt);
+  const float f = (mt == -INFINITY) ? 0.f : fast_exp2(mt - M);
+  o.x = reduce_lane_bits<kGroupBit, false>(o.x * f);
+  o.y = reduce_lane_bits<kGroupBit, false>(o.y * f);
+  o.z = reduce_lane_bits<kGroupBit, false>(o.z * f);
+  o.w = reduce_lane_bits<kGroupBit, false>(o.w * f);
+  ls = reduce_lane_bits<kGroupBit, false>(ls * f);
+  if (grp == 0) {
+    const float inv = (nsb == 0) ? 0.f : 1.f / ls;
+    const size_t e = qh * D + 4 * quad;
+    if (a.out_bf16) {
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + e;
+      const uint32_t lo = f32_to_bf16_rne(o.x * inv) | ((uint32_t)f32_to_bf16_rne(o.y * inv) << 16);
+      const uint32_t hi = f32_to_bf16_rne(o.z * inv) | ((uint32_t)f32_to_bf16_rne(o.w * inv) << 16);
+      *reinterpret_cast<uint2*>(op) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + e) =
+          make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    }
+    if (quad == 0 && a.lse != nullptr)
+      a.lse[qh] = (nsb == 0) ? -INFINITY : (M + __log2f(ls)) * kLn2;
   }
 }
 
@@ -1571,11 +1551,14 @@ hipError_t launch_split_kv_decode(int D, int G, int kv_format, bool paged, int B
 }
 
 hipError_t launch_lse_combine(int D, int B, const CombineArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)a.Hq, (unsigned)B);
+  const int64_t rows64 = (int64_t)B * a.Hq;
+  if (rows64 > INT32_MAX) return hipErrorInvalidValue;
+  const int rows = (int)rows64;
+  dim3 grid((unsigned)((rows + kCombineRows - 1) / kCombineRows));
   if (D == 128)
-    hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineThreads), 0, st, a);
+    hipLaunchKernelGGL(lse_combine_kernel<128>, grid, dim3(kCombineThreads), 0, st, a, rows);
   else if (D == 64)
-    hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineThreads), 0, st, a);
+    hipLaunchKernelGGL(lse_combine_kernel<64>, grid, dim3(kCombineThreads), 0, st, a, rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
