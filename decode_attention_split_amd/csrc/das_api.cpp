@@ -267,7 +267,6 @@ int run_phase2(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Smax, int
                const Checked& c, hipStream_t st) {
   if (c.ns <= 1) return DAS_OK;
   das::CombineArgs a{};
-  a.seq_lens = seq_lens;
   const char* ws = static_cast<const char*>(workspace);
   a.ws_o = reinterpret_cast<const float*>(ws + ws_o_offset());
   a.ws_ml = reinterpret_cast<const float*>(ws + ws_ml_offset(B, Hq, c.ns, D));

@@ -77,8 +77,7 @@ constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
 
 // Phase 2 (same post, §3 phase 2).  One workgroup per (query head, batch row).
 struct CombineArgs {
-  const int32_t* seq_lens;
-  const float* ws_o;
+  const float* ws_o;         // every slot written by phase 1 (empty splits: max -inf)
   const float* ws_ml;
   int32_t Hq, Smax, chunk, ns;   // chunk: rows per block, as in SplitArgs
   void* out;

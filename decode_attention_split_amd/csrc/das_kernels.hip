@@ -459,9 +459,18 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // chunk s (chunk * ns >= Smax, so every row has a split).
   const int n_chunks = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
   const int nsb = min(a.ns, n_chunks);                // splits this sequence uses
-  // An empty split exits at once; phase 2 never reads it.  With the fused
-  // merge, split 0 of an empty sequence stays to write out = 0, lse = -inf.
-  if (!a.direct && s >= n_chunks && !(a.fused && s == 0)) return;
+  // An empty split exits at once.  With the fused merge nothing reads its
+  // slots (split 0 of an empty sequence stays to write out = 0, lse = -inf);
+  // otherwise it marks its slots empty (max -inf, sum 0: the merge's
+  // identity), so that the separate phase-2 kernel reads every slot without
+  // first reading the sequence's length.
+  if (!a.direct && s >= n_chunks && !(a.fused && s == 0)) {
+    if (!a.fused && tid < G) {
+      const size_t row = ((size_t)b * a.Hq + (size_t)g * G + tid) * a.ns + s;
+      *reinterpret_cast<float2*>(a.ws_ml + 2 * row) = make_float2(-INFINITY, 0.f);
+    }
+    return;
+  }
 
   unsigned char* kt = smem + wave * kWaveBytes;
   float* pt = reinterpret_cast<float*>(kt + kKTileBytes);   // G <= 2
@@ -1227,9 +1236,20 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     const unsigned int prev = atomicAdd(cnt, 1u);
     const bool last = prev == (unsigned int)(nsb - 1);
     if (last) atomicExch(cnt, 0u);  // leave the counter at zero for the next call
-    s_last = last;
+    // A count of nsb or more is impossible in a workspace whose counters
+    // started at zero: the caller broke that precondition.  Fail loudly.
+    s_last = last ? 1 : (prev >= (unsigned int)nsb ? 2 : 0);
   }
   __syncthreads();
+  if (s_last == 2) {
+    // NaN outputs (and LSE) for this (b, kv-head), instead of stale ones
+    for (int i = tid; i < G * D / 4; i += kThreads) {
+      const float nan = __builtin_nanf("");
+      store_out4(a, qh0 * D + 4 * i, nan, nan, nan, nan);
+    }
+    if (tid < G && a.lse != nullptr) a.lse[qh0 + tid] = __builtin_nanf("");
+    return;
+  }
   if (!s_last) return;
 
   // One thread per (split group, head, float4 quad): lane = grp * kGroupLanes
@@ -1332,10 +1352,11 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kCombineRows + (threadIdx.x >> 6);   // b * Hq + h
   if (row >= rows) return;
-  const int b = row / a.Hq;
   const int quad = lane % kQuads, grp = lane / kQuads;
-  const int L = clamp_len(a.seq_lens[b], a.Smax);
-  const int nsb = min(a.ns, (L + a.chunk - 1) / a.chunk);  // splits this sequence used
+  // Every slot of the plan is read: phase 1 wrote each split's partial, and
+  // marked the splits its sequence does not reach empty (max -inf, sum 0);
+  // their partial rows were never written and are not used.
+  const int nsb = a.ns;
   const size_t qh = (size_t)row;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml + qh * a.ns * 2);
   const float4* po = reinterpret_cast<const float4*>(a.ws_o + qh * a.ns * D) + quad;
@@ -1351,16 +1372,18 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
       st[k] = c < nsb ? ml[c] : make_float2(-INFINITY, 0.f);
       pr[k] = c < nsb ? po[(size_t)c * kQuads] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float bm = st[0].x;   // finite: split c0 < nsb is in the batch
+    float bm = st[0].x;
 #pragma unroll
     for (int k = 1; k < kCombineBatch; ++k) bm = fmaxf(bm, st[k].x);
+    if (bm == -INFINITY) continue;   // only empty splits in this batch
     const float mn = fmaxf(mt, bm);
-    const float alpha = fast_exp2(mt - mn);   // 0 on the first batch
+    const float alpha = fast_exp2(mt - mn);   // 0 while nothing has been merged
     o.x *= alpha; o.y *= alpha; o.z *= alpha; o.w *= alpha;
     ls *= alpha;
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
-      const float w = fast_exp2(st[k].x - mn);   // 0 for the padding slots
+      if (st[k].x == -INFINITY) continue;   // an empty split: its row was never written
+      const float w = fast_exp2(st[k].x - mn);
       o.x = fmaf(w, pr[k].x, o.x);
       o.y = fmaf(w, pr[k].y, o.y);
       o.z = fmaf(w, pr[k].z, o.z);
@@ -1379,7 +1402,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
   o.w = reduce_lane_bits<kGroupBit, false>(o.w * f);
   ls = reduce_lane_bits<kGroupBit, false>(ls * f);
   if (grp == 0) {
-    const float inv = (nsb == 0) ? 0.f : 1.f / ls;
+    const float inv = (M == -INFINITY) ? 0.f : 1.f / ls;   // an empty sequence: out = 0
     const size_t e = qh * D + 4 * quad;
     if (a.out_bf16) {
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + e;
@@ -1391,7 +1414,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
           make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     }
     if (quad == 0 && a.lse != nullptr)
-      a.lse[qh] = (nsb == 0) ? -INFINITY : (M + __log2f(ls)) * kLn2;
+      a.lse[qh] = (M == -INFINITY) ? -INFINITY : (M + __log2f(ls)) * kLn2;
   }
 }
 

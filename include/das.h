@@ -166,7 +166,12 @@ size_t das_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t Sm
  * instead (as das_lse_combine).
  * Workspace precondition: its first DAS_WORKSPACE_COUNTER_BYTES must be zero
  * before the workspace is first used (allocate it zero-filled); every
- * completed call leaves them zero again, whatever the shape.
+ * completed call leaves them zero again, whatever the shape.  A counter the
+ * merge finds at or above the number of splits (a workspace that was never
+ * zeroed) turns that (b, kv-head)'s outputs and LSE into NaN; a smaller
+ * nonzero count (left by a call that never finished) cannot be told from a
+ * valid one and gives wrong outputs.  das_decode_attention_noalloc manages
+ * its own workspace.
  */
 int das_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
@@ -183,6 +188,8 @@ int das_decode_attention(const void* q, const void* k_cache, const void* v_cache
  * directly.  It never touches the workspace's arrival counters.
  * das_split_kv_decode + das_lse_combine computes what das_decode_attention
  * computes, with phase 2 as a separate kernel (sums may round differently).
+ * Every split slot of the plan is written: the partial of a split that
+ * holds rows, or an empty mark (max -inf, sum 0) for one past its sequence.
  */
 int das_split_kv_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
@@ -299,10 +306,11 @@ int das_decode_attention_paged(const void* q, const void* k_pool, const void* v_
 /*
  * Phase 2 alone ([FD++] §3, phase 2): merges the partial results that
  * das_split_kv_decode left in `workspace` (same B, Hq, Hkv, Smax, D,
- * num_splits, seq_lens) into out / lse_out.  Per (b, h): M = max of the
- * split maxima, w_c = exp(m_c - M), out = sum w_c o_c / sum w_c l_c,
- * lse = M + ln(sum w_c l_c).  A no-op returning DAS_OK when the plan has a
- * single split.
+ * num_splits) into out / lse_out.  Per (b, h): M = max of the split maxima,
+ * w_c = exp(m_c - M), out = sum w_c o_c / sum w_c l_c, lse = M + ln(sum w_c
+ * l_c).  Phase 1 marks the splits a sequence does not reach as empty (max
+ * -inf, sum 0), so seq_lens is checked (non-null, aligned) but not read.  A
+ * no-op returning DAS_OK when the plan has a single split.
  */
 int das_lse_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t Smax,
                     int32_t D, int32_t num_splits, const void* workspace,

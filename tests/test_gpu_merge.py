@@ -196,3 +196,26 @@ def test_fused_merge_ignores_whatever_the_partial_slots_held():
     assert torch.equal(got[0], want_o) and torch.equal(got[1], want_l), "after another plan"
     counters = ws[:cb].view(torch.int32)
     assert int(torch.count_nonzero(counters)) == 0
+
+
+def test_counters_left_nonzero_fail_loudly():
+    """A workspace whose arrival counters were never zeroed (here set, from
+    the host, to a count no call can reach) turns the fused merge's outputs
+    into NaN instead of leaving stale ones; once zeroed, the same workspace
+    gives the exact result again."""
+    cfg = workloads.custom_config(2, 32, 8, 128, 5000)
+    x = workloads.make_inputs(cfg, 12, seq_lens=(5000, 3100))
+    q, k, v, sl = upload(x)
+    ns = 9
+    need = das.das_decode_workspace_bytes(2, 32, 8, 5000, 128, ns)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    cb = das.DAS_WORKSPACE_COUNTER_BYTES
+    ws[:cb].view(torch.int32).fill_(0x7FFF0000)
+    out, lse = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(out)) and torch.all(torch.isnan(lse)), "garbage counters: NaN"
+    ws[:cb].zero_()
+    out, lse = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    check_f32(out, lse, *oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale), "after zeroing")
+    assert int(torch.count_nonzero(ws[:cb])) == 0
