@@ -388,10 +388,19 @@ class Workload:
 
     def event_us(self, calls, n: int, warmup: int) -> float:
         """Average µs per call over n back-to-back launches, from a pair of HIP
-        events on the launch stream (torch's current stream)."""
+        events on the launch stream (torch's current stream).  The warm-up is
+        at least `warmup` calls and at least 20 ms of them, so that a row
+        measured after the GPU sat idle (the CPU baseline runs before the
+        table) does not catch it with its clocks still low."""
         torch = self.torch
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t0 < 0.02:
             calls[i % len(calls)]()
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()   # keep the host clock in step with the GPU
+        warmup = i
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
