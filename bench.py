@@ -17,8 +17,9 @@ the same calls replayed from one HIP graph and the median of calls issued
 one at a time after a cache flush; the fp64 CPU oracle's throughput on a
 bounded sample of the same workload (the reported CPU baseline); and, in
 ``config.per_config``, every named config timed in the same process
-(automatic plan with fp32 and bf16 output, and one split).  Progress goes
-to stderr.
+(bf16 K/V: automatic plan with fp32 and bf16 output, and one split; E4M3
+and INT4 caches and page pools with the automatic plan).  Progress goes to
+stderr.
 """
 from __future__ import annotations
 
@@ -285,10 +286,9 @@ class Workload:
         self.quant = quant = fp8 or int4      # codes plus fp32 scales
         self.paged = None
         if paged:
-            if int4:
-                sys.exit("bench.py: there is no paged INT4 cache")
             layout = workloads.PAGED_HND if paged_layout == "hnd" else workloads.PAGED_NHD
-            self.paged = workloads.make_paged_inputs(cfg, 42 + config, paged, layout, fp8=fp8)
+            self.paged = workloads.make_paged_inputs(cfg, 42 + config, paged, layout, fp8=fp8,
+                                                     int4=int4, base=x)
             x = self.paged.base
         elif x is None:
             if int4:
@@ -315,8 +315,13 @@ class Workload:
         k_scale = v_scale = None
         alloc = x.k.nbytes + x.v.nbytes
         if quant:
-            k_scale = torch.from_numpy(x.k_scale).to(dev)
-            v_scale = torch.from_numpy(x.v_scale).to(dev)
+            if int4 and self.paged is not None:
+                # an INT4 pool's row scales live in pools laid out like it
+                k_scale = torch.from_numpy(self.paged.k_scale_pool).to(dev)
+                v_scale = torch.from_numpy(self.paged.v_scale_pool).to(dev)
+            else:
+                k_scale = torch.from_numpy(x.k_scale).to(dev)
+                v_scale = torch.from_numpy(x.v_scale).to(dev)
             if int4:
                 alloc += x.k_scale.nbytes + x.v_scale.nbytes
         src_k, src_v = ((self.paged.k_pool, self.paged.v_pool) if self.paged is not None
@@ -328,6 +333,8 @@ class Workload:
         self.table = None
         if self.paged is not None:
             alloc = self.paged.k_pool.nbytes + self.paged.v_pool.nbytes
+            if int4:
+                alloc += self.paged.k_scale_pool.nbytes + self.paged.v_scale_pool.nbytes
             self.table = torch.from_numpy(self.paged.block_table).to(dev)
         self.copies = copies or max(1, min(16, math.ceil(4 * LLC_BYTES / alloc)))
         self.ks, self.vs = [k0], [v0]
@@ -366,8 +373,8 @@ class Workload:
             return [das.prepare_decode_paged(self.q, self.ks[c], self.vs[c], self.table, self.sl,
                                              self.x.scale, self.paged.page_size,
                                              self.paged.layout, out, lse, splits, ws,
-                                             stream=stream, k_scale=self.k_scale,
-                                             v_scale=self.v_scale)
+                                             stream=stream, k_scale=self.kss[c],
+                                             v_scale=self.vss[c], kv_dtype=self.kv_code)
                     for c in range(self.copies)]
         if self.quant:
             name = ("das_decode_attention_int4" if self.kv_dtype == "int4"
@@ -386,12 +393,16 @@ class Workload:
         return (torch.empty((self.B, self.Hq, self.D), dtype=dt, device=self.q.device),
                 torch.empty((self.B, self.Hq), dtype=torch.float32, device=self.q.device))
 
-    def event_us(self, calls, n: int, warmup: int) -> float:
-        """Average µs per call over n back-to-back launches, from a pair of HIP
-        events on the launch stream (torch's current stream).  The warm-up is
-        at least `warmup` calls and at least 20 ms of them, so that a row
-        measured after the GPU sat idle (the CPU baseline runs before the
-        table) does not catch it with its clocks still low."""
+    def event_us(self, calls, n: int, warmup: int, reps: int = 3) -> float:
+        """µs per call: the median over `reps` runs of the average over n
+        back-to-back launches, each run timed by a pair of HIP events on the
+        launch stream (torch's current stream).  The warm-up is at least
+        `warmup` calls and at least 20 ms of them, so that a row measured
+        after the GPU sat idle (the CPU baseline runs before the table) does
+        not catch it with its clocks still low; the median drops a run that
+        is slow for other reasons (the first run on the large varlen cache
+        after other workloads ran measures about 4 % slow, the next ones at
+        the steady rate)."""
         torch = self.torch
         t0 = time.perf_counter()
         i = 0
@@ -400,16 +411,19 @@ class Workload:
             i += 1
             if i % 8 == 0:
                 torch.cuda.synchronize()   # keep the host clock in step with the GPU
-        warmup = i
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n):
-            calls[(warmup + i) % len(calls)]()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3
+        runs = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                calls[i % len(calls)]()
+                i += 1
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) / n * 1e3)
+        return sorted(runs)[len(runs) // 2]
 
     def row(self, splits: int, out_dtype: str, n: int, warmup: int) -> dict:
         """One line of the per-config table."""
@@ -417,38 +431,77 @@ class Workload:
         us = self.event_us(self.calls(splits, out, lse), n, warmup)
         ns, chunk = self.plan(splits)
         gbs = self.kv_bytes / (us * 1e-6) / 1e9
-        return {"workload": self.cfg.name, "G": self.Hq // self.Hkv,
-                "splits": "auto" if splits == 0 else splits,
+        pool = None
+        if self.paged is not None:
+            pool = (f"P={self.paged.page_size} "
+                    f"{'HND' if self.paged.layout == self.das.DAS_PAGED_HND else 'NHD'}")
+        return {"workload": self.cfg.name, "G": self.Hq // self.Hkv, "kv_dtype": self.kv_dtype,
+                "paged": pool, "splits": "auto" if splits == 0 else splits,
                 "plan": f"{ns} x {chunk}", "merge": fused_merge(self.B, self.Hkv, ns, self.cus),
                 "out_dtype": out_dtype, "kv_bytes": self.kv_bytes, "us_per_call": round(us, 2),
-                "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "launches": n}
+                "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "launches": f"median of 3 x {n}"}
+
+
+# Page pools of the table's paged rows: page size and layout per cache format.
+TABLE_POOLS = {"bf16": (256, "hnd"), "fp8": (64, "hnd"), "int4": (256, "hnd")}
 
 
 def per_config_table(args, headline: "Workload") -> list:
-    """Every named config (bf16 K/V) in this process: the automatic plan with
-    fp32 output, the same with bf16 output, and one split (the unsplit
-    kernel the pages start from) -- µs per call by HIP events over
-    args.table_steps back-to-back launches."""
+    """Every named config in this process, µs per call by HIP events (the
+    median of three runs of args.table_steps back-to-back launches):
+    - bf16 K/V: the automatic plan with fp32 output, the same with bf16
+      output, and one split (the unsplit kernel the pages start from);
+    - the 32K-token cache of config 1 with other GQA groups: Hq = 8 and 16
+      (G = 1, 2: the vector-ALU path at long context, the per-head grid of
+      [FD++] §2) and Hq = 128 (G = 16);
+    - the E4M3 and INT4 caches on configs 1-4, and page pools of each
+      format ([FD++] §4 and §6) on configs 1-3 (bf16) and 3 (all three),
+      with the automatic plan and fp32 output."""
     import torch
 
     import workloads
 
     rows = []
-    # the named configs, then the 32K-token cache of config 1 with other
-    # GQA groups: Hq = 8 and 16 (G = 1, 2: the vector-ALU path at long
-    # context, the per-head grid of [FD++] §2) and Hq = 128 (G = 16)
-    jobs = [(idx, 0) for idx in range(len(workloads.CONFIGS))] + [(1, 8), (1, 16), (1, 128)]
-    for idx, hq in jobs:
-        if headline is not None and idx == args.config and headline.kv_dtype == "bf16" \
-                and headline.paged is None and hq == args.hq:
-            w = headline
-        else:
-            w = Workload(args, idx, hq=hq)
-        variants = ((0, "f32"), (0, "bf16"), (1, "f32")) if not hq else ((0, "f32"),)
+    n = len(workloads.CONFIGS)
+
+    def run(w, variants):
         for splits, out_dtype in variants:
             rows.append(w.row(splits, out_dtype, args.table_steps, args.table_warmup))
-        print(f"bench: table {w.cfg.name} done", file=sys.stderr, flush=True)
+        label = w.cfg.name + ("" if w.kv_dtype == "bf16" else f" {w.kv_dtype}") + \
+            ("" if w.paged is None else " paged")
+        print(f"bench: table {label} done", file=sys.stderr, flush=True)
+
+    def paged_rows(kv, idx, x):
+        P, layout = TABLE_POOLS[kv]
+        p = Workload(args, idx, kv, P, layout, x=x)
+        run(p, ((0, "f32"),))
+        del p
+
+    auto = ((0, "f32"),)
+    for idx in range(n):
+        if headline is not None and idx == args.config and headline.kv_dtype == "bf16" \
+                and headline.paged is None and not args.hq:
+            w = headline
+        else:
+            w = Workload(args, idx)
+        run(w, ((0, "f32"), (0, "bf16"), (1, "f32")))
+        if 1 <= idx <= 3:   # the same rows from a bf16 page pool
+            paged_rows("bf16", idx, w.x)
         if w is not headline:
+            del w
+        torch.cuda.empty_cache()
+    for hq in (8, 16, 128):
+        w = Workload(args, 1, hq=hq)
+        run(w, auto)
+        del w
+        torch.cuda.empty_cache()
+    for kv in ("fp8", "int4"):
+        for idx in range(1, n):
+            w = Workload(args, idx, kv)
+            run(w, auto)
+            if idx == 3:
+                paged_rows(kv, idx, w.x)
             del w
             torch.cuda.empty_cache()
     return rows

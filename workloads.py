@@ -437,22 +437,30 @@ class PagedInputs:
 
 def make_paged_inputs(cfg: Config, seed: int, page_size: int, layout: int = PAGED_HND,
                       smax: Optional[int] = None, seq_lens: Optional[Sequence[int]] = None,
-                      spare_pages: int = 3, fp8: bool = False, int4: bool = False) -> PagedInputs:
+                      spare_pages: int = 3, fp8: bool = False, int4: bool = False,
+                      base=None) -> PagedInputs:
     """``make_inputs`` (or ``make_fp8_inputs`` / ``make_int4_inputs``; same
     seed, same rows), scattered into a page pool.  An INT4 cache's row scales
     go into scale pools laid out like the code pools (same pages, same
-    table); spare rows hold code byte 0x88 and a NaN scale."""
+    table); spare rows hold code byte 0x88 and a NaN scale.  ``base``: inputs
+    of that format already drawn with this seed (``cfg``, ``smax`` and
+    ``seq_lens`` are then not used to draw them again)."""
     if fp8 and int4:
         raise ValueError("one cache format at a time")
     if int4:
-        base = make_int4_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        base = base if base is not None else make_int4_inputs(cfg, seed, smax=smax,
+                                                              seq_lens=seq_lens)
         fill = np.uint8(0x88)
     elif fp8:
-        base = make_fp8_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        base = base if base is not None else make_fp8_inputs(cfg, seed, smax=smax,
+                                                             seq_lens=seq_lens)
         fill = E4M3_NAN
     else:
-        base = make_inputs(cfg, seed, smax=smax, seq_lens=seq_lens)
+        base = base if base is not None else make_inputs(cfg, seed, smax=smax,
+                                                         seq_lens=seq_lens)
         fill = BF16_QNAN
+    if base.k.dtype != (np.uint8 if (fp8 or int4) else np.uint16):
+        raise ValueError("base inputs are not of the requested cache format")
     k_pool, v_pool, table = scatter_to_pages(base.k, base.v, base.seq_lens, page_size, layout,
                                              seed, fill, spare_pages)
     ks_pool = vs_pool = None
