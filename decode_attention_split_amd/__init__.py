@@ -23,6 +23,10 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdas.so")
+# The debug build: the same library with every LDS buffer filled with NaN
+# bytes when it stops being live (a read that races its write then returns
+# NaN instead of stale values).  Tests only; nothing here loads it by itself.
+DEBUG_LIB_PATH = os.path.join(_HERE, "libdas_debug.so")
 
 DAS_OK, DAS_EINVAL, DAS_ENOTSUP, DAS_EWORKSPACE, DAS_ELAUNCH = 0, -1, -2, -3, -4
 DAS_F32, DAS_BF16, DAS_E4M3, DAS_INT4 = 0, 1, 2, 3
@@ -52,6 +56,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at ``path`` (libdas.so, or the debug
+    build libdas_debug.so) with the C signatures declared, without making it
+    the one the entry points below call.  Raises if it is missing."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
                            "(hipcc --offload-arch=gfx950) first")
@@ -86,7 +98,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.das_merge_attn_states.restype = ctypes.c_int
     lib.das_strerror.argtypes = [ctypes.c_int]
     lib.das_strerror.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 
@@ -245,8 +256,8 @@ class PreparedCall:
     pointers and sizes, skipping the Python-side shape checks.  It keeps the
     tensors it points to alive."""
 
-    def __init__(self, name: str, args: tuple, keep: tuple):
-        self._fn = getattr(load_library(), name)
+    def __init__(self, name: str, args: tuple, keep: tuple, lib: Optional[ctypes.CDLL] = None):
+        self._fn = getattr(lib if lib is not None else load_library(), name)
         self._name = name
         self._args = args
         self._keep = keep
@@ -255,6 +266,11 @@ class PreparedCall:
         rc = self._fn(*self._args)
         if rc != DAS_OK:
             raise DasError(rc, self._name)
+
+    def on_library(self, lib: ctypes.CDLL) -> "PreparedCall":
+        """The same call (same pointers and sizes) into another build of the
+        library, e.g. one from open_library."""
+        return PreparedCall(self._name, self._args, self._keep, lib)
 
 
 def prepare_decode(fn_name: str, q, k_cache, v_cache, seq_lens, scale: float,

@@ -21,6 +21,16 @@ namespace das {
 #ifndef DAS_MIN_WAVES_PER_EU
 #define DAS_MIN_WAVES_PER_EU 2  // waves per SIMD the register allocator must allow
 #endif
+// Debug build (libdas_debug.so): 1 fills each wave's LDS tile region with
+// 0xFF bytes (NaN as bf16, E4M3 and fp32) before its first use and after
+// every tile it has finished reading, and the per-wave statistics slots with
+// NaN before the stream.  A read that is not ordered after the write it
+// needs (a missing wait for a load into LDS, a missing barrier before the
+// cross-wave merge) then returns NaN instead of plausible stale values.
+// Results are otherwise bit-for-bit those of the regular build.
+#ifndef DAS_DEBUG_LDS_POISON
+#define DAS_DEBUG_LDS_POISON 0
+#endif
 
 constexpr int kWaves = DAS_WAVES;
 constexpr int kThreads = 64 * kWaves;

@@ -283,12 +283,31 @@ constexpr int vmcnt_imm(int n) {
   return (n & 0xF) | (((n >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// s_waitcnt immediate that waits until every LDS (and scalar memory)
+// operation of the wave has completed.
+constexpr int lgkmcnt0_imm() { return 0xF | (0x3 << 14) | (0x7 << 4); }
+
 // Orders this wave's LDS accesses before the point against those after it
 // (each wave owns its tile region, so no workgroup barrier is needed).
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Debug build: fills kBytes (a multiple of 16) of this wave's LDS at p with
+// 0xFF bytes, ordered after the wave's earlier LDS reads and completed before
+// anything after it (including loads that write LDS directly) can land.
+template <int kBytes>
+__device__ __forceinline__ void poison_wave_lds(unsigned char* p, int lane) {
+  static_assert(kBytes % 16 == 0, "16-byte stores");
+  if constexpr (DAS_DEBUG_LDS_POISON) {
+    wave_lds_fence();
+    for (int off = 16 * lane; off < kBytes; off += 1024)
+      *reinterpret_cast<uint4*>(p + off) = make_uint4(~0u, ~0u, ~0u, ~0u);
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    wave_lds_fence();
+  }
 }
 
 // Bytes of one cached row of D elements.
@@ -474,6 +493,8 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
 
   unsigned char* kt = smem + wave * kWaveBytes;
   float* pt = reinterpret_cast<float*>(kt + kKTileBytes);   // G <= 2
+  // Per-wave running max and sum per head at the end of the stream.
+  __shared__ float wst_ml[kWaves * 2 * G];
 
   // The sequence's valid rows of K and V as bounds-checked buffers: loads
   // past row L return zeros, and the rows beyond seq_lens are never read.
@@ -1006,6 +1027,11 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   VReg vr[kLoads];
   TileRegs tr;
   int page_next = 0;
+  // debug build: the wave's tile region and statistics slots start as NaN
+  poison_wave_lds<kWaveBytes>(kt, lane);
+  if constexpr (DAS_DEBUG_LDS_POISON) {
+    if (lane < 2 * G) wst_ml[wave * 2 * G + lane] = __builtin_nanf("");
+  }
   if (r0 < row_end) {
     const int page = kPaged ? page_of(r0) : 0;
     if (kPaged && r0 + stride < row_end) page_next = page_of(r0 + stride);
@@ -1066,10 +1092,12 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         fetch_tile(rn, tr, page);
       }
       process_tile(r0, vr, kt);
+      poison_wave_lds<kWaveBytes>(kt, lane);   // debug build: the tile is dead
     }
   } else {
     for (; r0 < row_end; r0 += stride) {
       process_tile(r0, vr, kt);
+      poison_wave_lds<kWaveBytes>(kt, lane);   // debug build: the tile is dead
       const int rn = r0 + stride;
       if (rn < row_end) {
         const int page = page_next;
@@ -1083,7 +1111,6 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // The wave's tiles are no longer needed, and no other wave touches them:
   // the state goes there without waiting for the others.  Layout [row
   // group][head][D] floats; max and sum per head in wst_ml.
-  __shared__ float wst_ml[kWaves * 2 * G];
   float* wst = reinterpret_cast<float*>(kt);
   if constexpr (kMfmaPv) {
     l_sum = reduce_lane_bits<4, false>(l_sum);  // lane n: head n's sum over the wave's rows

@@ -77,6 +77,49 @@ def test_merging_two_half_sequences_equals_whole():
     assert float(torch.max(torch.abs(mo - whole_o))) <= 5e-4
 
 
+def test_merge_is_associative_over_three_parts_of_a_sequence():
+    """Decode over three parts of the rows, merge them on the GPU in both
+    groupings ((a b) c and a (b c)): each equals the oracle's attention over
+    the whole sequence, and the two agree to rounding.  The merge is exact in
+    real arithmetic; the groupings differ in the fp32 rounding of the
+    intermediate state, above all of its LSE (half an ulp of |lse| each),
+    which enters a weight exp(lse - max): a relative change of the weights of
+    about ulp(|lse|), so of the output by that times max |o| of the parts."""
+    cfg = workloads.custom_config(3, 16, 4, 128, 3000, k_mult=4.0)
+    x = workloads.make_inputs(cfg, 78, seq_lens=(3000, 2500, 700))
+    q, k, v, sl = upload(x)
+    cuts = (0, 1000, 2000, 3000)
+    parts = []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        # rows [lo, hi) of each sequence (none where the sequence ends before lo)
+        part_len = torch.clamp(torch.clamp(sl, max=hi) - lo, min=0)
+        parts.append(das.das_decode_attention(q, k[:, :, lo:hi].contiguous(),
+                                              v[:, :, lo:hi].contiguous(), part_len, x.scale))
+    (ao, al), (bo, bl), (co, cl) = parts
+    ab = das.das_merge_attn_states(ao, al, bo, bl)
+    left = das.das_merge_attn_states(ab[0], ab[1], co, cl)
+    bc = das.das_merge_attn_states(bo, bl, co, cl)
+    right = das.das_merge_attn_states(ao, al, bc[0], bc[1])
+    torch.cuda.synchronize()
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    check_f32(left[0], left[1], *ref, "(a b) c")
+    check_f32(right[0], right[1], *ref, "a (b c)")
+    # the third sequence ends inside part a: parts b and c are empty there
+    # (lse -inf, the merge's identity), and both groupings give part a's state
+    for got in (left, right):
+        assert torch.allclose(got[0][2], ao[2], rtol=0, atol=1e-6)
+        assert torch.allclose(got[1][2], al[2], rtol=0, atol=1e-6)
+    lses = torch.cat([al, bl, cl])
+    lse_max = float(torch.max(torch.abs(lses[torch.isfinite(lses)])))
+    ulp = 2.0 ** (math.floor(math.log2(lse_max)) - 23)     # fp32 ulp at max |lse|
+    o_max = max(float(torch.max(torch.abs(t))) for t in (ao, bo, co))
+    d_o = float(torch.max(torch.abs(left[0] - right[0])))
+    d_l = float(torch.max(torch.abs(left[1] - right[1])))
+    note(f"  groupings differ by {d_o:.3e} (out), {d_l:.3e} (lse); ulp(max|lse|) {ulp:.3e}")
+    assert d_o <= 4 * ulp * o_max + 2.0 ** -20 * o_max
+    assert d_l <= 4 * ulp
+
+
 def test_two_phase_entry_points_match_the_fused_call():
     """das_split_kv_decode + das_lse_combine (two kernels) computes what the fused
     das_decode_attention computes; only the merge's summation order differs."""

@@ -38,6 +38,20 @@ def test_library_exports_every_declared_symbol(lib):
         getattr(lib, name)
 
 
+def test_debug_build_exports_the_same_symbols(lib):
+    """libdas_debug.so (the LDS-poisoning debug build, made by the same
+    build step) loads and exports every declared entry point too."""
+    declared = _header_functions()
+    dbg = das.open_library(das.DEBUG_LIB_PATH)
+    nm = subprocess.run(["nm", "-D", "--defined-only", das.DEBUG_LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, f"{name} not exported by the debug build"
+        getattr(dbg, name)
+    assert das.load_library() is lib   # opening another build leaves the loaded one in place
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4):
         assert das.das_strerror(code)
