@@ -473,7 +473,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     }
   }
 
-  const int L = clamp_len(a.seq_lens[b], a.Smax);
+  // (the same for every lane: kept in a scalar register, so that everything
+  // derived from it -- the stream bounds, the buffer offsets -- is too)
+  const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Smax));
   // The sequence's rows are cut into chunks of a.chunk rows; split s owns
   // chunk s (chunk * ns >= Smax, so every row has a split).
   const int n_chunks = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
@@ -626,6 +628,11 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         srow = r0 - p0;
       }
     }
+    // The tile offsets are the same for every lane.  Said so explicitly: the
+    // compiler otherwise keeps the offset's induction variable in a vector
+    // register and wraps every load in a loop over its distinct values.
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    srow = __builtin_amdgcn_readfirstlane(srow);
     if constexpr (kInt4) {
       row_ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           sk, (lane % kT) * scale_row * 4, srow * scale_row * 4, 0));
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   struct TileRegs {
     uint4 k[kMfmaPv ? kKLoads : 1];
     uint4 v[kMfmaPv ? kKLoads : 1];
-    float sc;
+    float ksc, vsc;   // INT4: the K and V scales of row lane % kT
   };
   auto fetch_tile = [&](int r0, TileRegs& t, int page) {
     __amdgpu_buffer_rsrc_t rk = rk_seq, rv = rv_seq, sk = rks, sv = rvs;
@@ -683,13 +690,19 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         srow = r0 - p0;
       }
     }
+    soff = __builtin_amdgcn_readfirstlane(soff);   // the same for every lane
+    srow = __builtin_amdgcn_readfirstlane(srow);
     if constexpr (kInt4) {
-      if (lane < kT)
-        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            sk, lane * scale_row * 4, srow * scale_row * 4, 0));
-      else
-        t.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            sv, (lane - kT) * scale_row * 4, srow * scale_row * 4, 0));
+      // Both scales of row lane % kT, each through a wave-uniform
+      // descriptor (stage_tile keeps the K ones in lanes [0, kT), the V ones
+      // in the others).  Choosing the descriptor per lane would make it
+      // divergent, and the compiler then loops over its distinct values with
+      // a wait for every outstanding load -- the tile prefetch included --
+      // inside the loop; choosing between the two values here would wait for
+      // them at once.
+      const int soff_s = srow * scale_row * 4, voff_s = (lane % kT) * scale_row * 4;
+      t.ksc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sk, voff_s, soff_s, 0));
+      t.vsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sv, voff_s, soff_s, 0));
     }
 #pragma unroll
     for (int m = 0; m < kKLoads; ++m) {
@@ -714,7 +727,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       *reinterpret_cast<uint4*>(kbuf + kKTileBytes + m * 1024 + 16 * lane) = t.v[m];
     // INT4: the K row scales go in with the logit scale folded in
     if constexpr (kInt4)
-      reinterpret_cast<float*>(kbuf + 2 * kKTileBytes)[lane] = lane < kT ? t.sc * c2 : t.sc;
+      reinterpret_cast<float*>(kbuf + 2 * kKTileBytes)[lane] = lane < kT ? t.ksc * c2 : t.vsc;
     wave_lds_fence();
   };
 
