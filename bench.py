@@ -399,10 +399,8 @@ class Workload:
         launch stream (torch's current stream).  The warm-up is at least
         `warmup` calls and at least 20 ms of them, so that a row measured
         after the GPU sat idle (the CPU baseline runs before the table) does
-        not catch it with its clocks still low; the median drops a run that
-        is slow for other reasons (the first run on the large varlen cache
-        after other workloads ran measures about 4 % slow, the next ones at
-        the steady rate)."""
+        not catch it with its clocks still low; the median drops a single
+        run that something else on the GPU slowed."""
         torch = self.torch
         t0 = time.perf_counter()
         i = 0
@@ -458,8 +456,6 @@ def per_config_table(args, headline: "Workload") -> list:
     - the E4M3 and INT4 caches on configs 1-4, and page pools of each
       format ([FD++] §4 and §6) on configs 1-3 (bf16) and 3 (all three),
       with the automatic plan and fp32 output."""
-    import torch
-
     import workloads
 
     rows = []
@@ -478,6 +474,9 @@ def per_config_table(args, headline: "Workload") -> list:
         run(p, ((0, "f32"),))
         del p
 
+    # Freed device memory stays with torch's allocator (no empty_cache): memory
+    # handed back to the driver is cleared by it in the background, which
+    # slows the next rows' HBM stream for tens of milliseconds.
     auto = ((0, "f32"),)
     for idx in range(n):
         if headline is not None and idx == args.config and headline.kv_dtype == "bf16" \
@@ -490,12 +489,10 @@ def per_config_table(args, headline: "Workload") -> list:
             paged_rows("bf16", idx, w.x)
         if w is not headline:
             del w
-        torch.cuda.empty_cache()
     for hq in (8, 16, 128):
         w = Workload(args, 1, hq=hq)
         run(w, auto)
         del w
-        torch.cuda.empty_cache()
     for kv in ("fp8", "int4"):
         for idx in range(1, n):
             w = Workload(args, idx, kv)
@@ -503,7 +500,6 @@ def per_config_table(args, headline: "Workload") -> list:
             if idx == 3:
                 paged_rows(kv, idx, w.x)
             del w
-            torch.cuda.empty_cache()
     return rows
 
 
