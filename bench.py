@@ -182,10 +182,20 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, ns: int):
+def counters_path(workload: str, kv_dtype: str = "bf16", page_size: int = 0,
+                  layout: str = "hnd") -> str:
+    """The committed counter summary of a workload, cache format and pool."""
+    name = "split_kv_decode" + ("_paged" if page_size else "") + \
+        {"bf16": "", "fp8": "_e4m3", "int4": "_int4"}[kv_dtype] + "_" + workload + \
+        (f"_p{page_size}_{layout}" if page_size else "") + "_counters.json"
+    return os.path.join(ROOT, "profiles", name)
+
+
+def measured_traffic(workload: str, ns: int, kv_dtype: str = "bf16", page_size: int = 0,
+                     layout: str = "hnd"):
     """HBM bytes per launch from the committed counter summary, when it was
     taken on the current kernel source and this workload; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"split_kv_decode_{workload}_counters.json")
+    path = counters_path(workload, kv_dtype, page_size, layout)
     try:
         with open(path) as fh:
             doc = json.load(fh)
@@ -646,8 +656,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if (quant or paged is not None or args.hq or args.splits
-                                or args.out_dtype != "f32") else measured_traffic(cfg.name, ns),
+            "traffic": None if (args.hq or args.splits or args.out_dtype != "f32")
+                       else measured_traffic(cfg.name, ns, args.kv_dtype, args.paged,
+                                             args.paged_layout),
             "kernel_us": round(kernel_ms * 1e3, 3),
         },
     }
