@@ -439,9 +439,13 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // 8, every sequence's first split would share XCD 0).  The padding splits
   // exit at once.
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  if (s >= a.ns) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  // The sequence length, read first and through the constant address space
+  // (the lengths are read-only for the whole kernel): a scalar load that
+  // goes out with the query loads below, before any branch.  Every K/V load
+  // waits for it, so the fewer round trips ahead of it the better.
+  const int len_in = ((const __attribute__((address_space(4))) int32_t*)a.seq_lens)[b];
 
   // ---- the query rows, loaded first: their latency overlaps that of the
   // sequence length and the issue of the first K/V tile ----
@@ -473,9 +477,15 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     }
   }
 
-  // (the same for every lane: kept in a scalar register, so that everything
-  // derived from it -- the stream bounds, the buffer offsets -- is too)
-  const int L = __builtin_amdgcn_readfirstlane(clamp_len(a.seq_lens[b], a.Smax));
+  // The length and the arguments the first K/V loads need are wanted here,
+  // after the query loads have gone out: not one round trip at a time
+  // further down, where the compiler would otherwise move their loads.
+  __asm__ volatile("" : : "s"(len_in), "s"(a.k), "s"(a.v), "s"(a.chunk), "s"(a.ns),
+                   "s"(a.Smax), "s"(a.Hkv), "s"(a.direct), "s"(a.fused));
+  if (s >= a.ns) return;   // a padding split of the odd grid
+  // wave-uniform, so everything derived from it -- the stream bounds, the
+  // buffer offsets -- is too
+  const int L = clamp_len(len_in, a.Smax);
   // The sequence's rows are cut into chunks of a.chunk rows; split s owns
   // chunk s (chunk * ns >= Smax, so every row has a split).
   const int n_chunks = (L + a.chunk - 1) / a.chunk;   // chunks holding valid rows
@@ -529,8 +539,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   float c2 = a.scale_log2e;
   float v_scale = 1.f;
   if constexpr (kFp8) {
-    c2 *= a.k_scale[g];
-    v_scale = a.v_scale[g];
+    // (read-only for the whole kernel: scalar loads, as the length)
+    c2 *= ((const __attribute__((address_space(4))) float*)a.k_scale)[g];
+    v_scale = ((const __attribute__((address_space(4))) float*)a.v_scale)[g];
   }
 
   // ---- query operand (filled from qraw once the first tile is issued) ----
