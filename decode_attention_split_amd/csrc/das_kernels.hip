@@ -477,6 +477,25 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
     }
   }
 
+  // Paged cache: the block-table entries of the pages this wave's tiles lie
+  // in, read with one vector load, one entry per lane (page_for, below),
+  // issued here so that their latency overlaps the length's.  Tile k of the
+  // wave (rows row_lo + wave*kT + k*stride ...) lies in the wave's page
+  // k >> tiles_per_entry; entry i is the page of its tile i << tiles_per_entry,
+  // i.e. table slot first_slot + i * slot_step.  Entries past the table row
+  // read as 0 (bounds-checked load) and are never used.
+  constexpr int kStrideShift = log2_int(kWaves * kT);
+  int tiles_per_entry = 0, first_slot = 0, slot_step = 0, entry_base = 0, table_lane = 0;
+  const __amdgpu_buffer_rsrc_t table_rsrc =
+      make_rsrc(kPaged ? a.block_table + (size_t)b * a.max_blocks : nullptr,
+                kPaged ? a.max_blocks * 4 : 0);
+  if constexpr (kPaged) {
+    tiles_per_entry = max(a.page_shift - kStrideShift, 0);
+    first_slot = (s * a.chunk + wave * kT) >> a.page_shift;
+    slot_step = max((kWaves * kT) >> a.page_shift, 1);
+    table_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        table_rsrc, (first_slot + lane * slot_step) * 4, 0, 0);
+  }
   // The length and the arguments the first K/V loads need are wanted here,
   // after the query loads have gone out: not one round trip at a time
   // further down, where the compiler would otherwise move their loads.
@@ -592,14 +611,18 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       kInt4, uint32_t, typename std::conditional<kFp8, uint2, uint4>::type>::type;
   // INT4, G <= 2: the K and V scales of this lane's row (lane % kT) of the tile
   float row_ks = 0.f, row_vs = 0.f;
-  // Paged cache: the block-table entry of the page holding row r.  The table
-  // is read-only for the whole kernel, so it is read through the constant
-  // address space, which makes this a scalar load that only its use waits
-  // for; the stream loop fetches the next tile's entry one tile ahead.
-  auto page_of = [&](int r) -> int {
-    const __attribute__((address_space(4))) int32_t* table =
-        (const __attribute__((address_space(4))) int32_t*)a.block_table;
-    return table[(size_t)b * a.max_blocks + (r >> a.page_shift)];
+  // Paged cache: the block-table entry of the page holding the wave's tile
+  // k (k = 0, 1, ... in stream order), a lane read of the entries loaded at
+  // the start; every 64 entries (a split longer than 64 of the wave's pages)
+  // the next 64 are loaded, a round trip the stream waits for once.
+  auto page_for = [&](int k) -> int {
+    const int e = k >> tiles_per_entry;
+    if (e >= entry_base + 64) {   // wave-uniform; k grows by one per call
+      entry_base += 64;
+      table_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
+          table_rsrc, (first_slot + (entry_base + lane) * slot_step) * 4, 0, 0);
+    }
+    return __builtin_amdgcn_readlane(table_lane, e - entry_base);
   };
 
   // G <= 2: K straight into the wave's LDS tile, V (and INT4 row scales)
@@ -1050,15 +1073,14 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   int r0 = row_lo + wave * kT;
   VReg vr[kLoads];
   TileRegs tr;
-  int page_next = 0;
+  int tile_k = 0;   // paged cache: index of the wave's tile at r0
   // debug build: the wave's tile region and statistics slots start as NaN
   poison_wave_lds<kWaveBytes>(kt, lane);
   if constexpr (DAS_DEBUG_LDS_POISON) {
     if (lane < 2 * G) wst_ml[wave * 2 * G + lane] = __builtin_nanf("");
   }
   if (r0 < row_end) {
-    const int page = kPaged ? page_of(r0) : 0;
-    if (kPaged && r0 + stride < row_end) page_next = page_of(r0 + stride);
+    const int page = kPaged ? page_for(0) : 0;
     if constexpr (kMfmaPv)
       fetch_tile(r0, tr, page);
     else
@@ -1107,27 +1129,19 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   // process the staged one.  G <= 2: process the tile in flight, then issue
   // the next one.
   if constexpr (kMfmaPv) {
-    for (; r0 < row_end; r0 += stride) {
+    for (; r0 < row_end; r0 += stride, ++tile_k) {
       stage_tile(tr, kt);
       const int rn = r0 + stride;
-      if (rn < row_end) {
-        const int page = page_next;
-        if (kPaged && rn + stride < row_end) page_next = page_of(rn + stride);
-        fetch_tile(rn, tr, page);
-      }
+      if (rn < row_end) fetch_tile(rn, tr, kPaged ? page_for(tile_k + 1) : 0);
       process_tile(r0, vr, kt);
       poison_wave_lds<kWaveBytes>(kt, lane);   // debug build: the tile is dead
     }
   } else {
-    for (; r0 < row_end; r0 += stride) {
+    for (; r0 < row_end; r0 += stride, ++tile_k) {
       process_tile(r0, vr, kt);
       poison_wave_lds<kWaveBytes>(kt, lane);   // debug build: the tile is dead
       const int rn = r0 + stride;
-      if (rn < row_end) {
-        const int page = page_next;
-        if (kPaged && rn + stride < row_end) page_next = page_of(rn + stride);
-        load_tile(rn, vr, kt, page);
-      }
+      if (rn < row_end) load_tile(rn, vr, kt, kPaged ? page_for(tile_k + 1) : 0);
     }
   }
 

@@ -73,6 +73,25 @@ def test_paged_small_shapes(D, G, layout):
 
 
 @pytest.mark.parametrize("layout", [HND, NHD], ids=["HND", "NHD"])
+@pytest.mark.parametrize("G,fmt", [(4, "bf16"), (1, "bf16"), (2, "int4"), (8, "int4")],
+                         ids=["G4-bf16", "G1-bf16", "G2-int4", "G8-int4"])
+def test_paged_long_splits_read_the_table_in_rounds(G, fmt, layout):
+    """A wave keeps the block-table entries of its pages in one register,
+    64 at a time: with 32-row pages and one split over 20,000 rows a wave
+    passes 79 pages, so the entries are loaded in two rounds (two splits: 40
+    pages, one round)."""
+    cfg = workloads.custom_config(2, 2 * G, 2, 128, 20000, k_mult=2.0)
+    x = workloads.make_paged_inputs(cfg, 8300 + G + layout, 32, layout, seq_lens=(20000, 16700),
+                                    int4=fmt == "int4")
+    ref = ref_paged(x)
+    t = upload_paged(x)
+    for ns in (1, 2):
+        note(f"case paged long split G={G} {fmt} layout={layout} num_splits={ns}")
+        out, lse = run_paged(x, ns, tensors=t)
+        check_f32(out, lse, *ref, f"paged long G={G} {fmt} L{layout} ns={ns}")
+
+
+@pytest.mark.parametrize("layout", [HND, NHD], ids=["HND", "NHD"])
 def test_paged_single_split_equals_contiguous_bitwise(layout):
     """With one split, the paged call streams the same rows in the same order
     as the contiguous call: bitwise the same result."""
