@@ -119,6 +119,38 @@ def test_many_forced_splits_and_empty_ones():
         check_f32(out, lse, *ref, f"forced ns={ns}")
 
 
+def test_largest_batch_grid():
+    """The largest batch the grid takes (B = 65,535 sequences, the grid's
+    third dimension), lengths 0 ... 16 including empty ones: one split each,
+    every output written directly."""
+    B = 65535
+    rng = np.random.Generator(np.random.PCG64(4200))
+    lens = rng.integers(0, 16, size=B, endpoint=True)
+    cfg = workloads.custom_config(B, 2, 1, 64, 16)
+    x = workloads.make_inputs_bulk(cfg, 4201, lens)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    note(f"case largest batch B={B}: plan {das.das_plan(B, 1, 2, 16, 64)}")
+    out, lse = run(x)
+    check_f32(out, lse, *ref, f"B={B}")
+
+
+def test_large_batch_many_split_workgroups():
+    """16,384 sequences of up to 320 rows, two splits each where the length
+    needs them: 32,768 split workgroups, phase 2 as the separate merge kernel
+    over 32,768 (b, query head) rows."""
+    B = 16384
+    rng = np.random.Generator(np.random.PCG64(4300))
+    lens = rng.integers(0, 320, size=B, endpoint=True)
+    cfg = workloads.custom_config(B, 2, 1, 64, 320)
+    x = workloads.make_inputs_bulk(cfg, 4301, lens)
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    ns, chunk = das.das_plan(B, 1, 2, 320, 64, 2)
+    note(f"case large batch B={B}: plan ns={ns} chunk={chunk}")
+    assert ns == 2
+    out, lse = run(x, 2)
+    check_f32(out, lse, *ref, f"B={B} ns=2")
+
+
 def _steer_keys(x, ramps):
     """Give every (batch row, kv-head) a designed logit profile along the
     sequence: valid row j of K becomes a quarter of its random value plus

@@ -195,6 +195,37 @@ def make_inputs(cfg: Config, seed: int, smax: Optional[int] = None,
     return Inputs(cfg, seed, q, k, v, lens, cfg.scale)
 
 
+def make_inputs_bulk(cfg: Config, seed: int, seq_lens: Sequence[int],
+                     smax: Optional[int] = None) -> Inputs:
+    """Like ``make_inputs`` for very large batches of short sequences: q, then
+    all valid rows of K (in (b, head, row, dim) order), then all of V, each
+    drawn in one call from one ``Generator(PCG64(seed))`` (``make_inputs``
+    draws every (b, head) from its own jumped stream, whose set-up dominates
+    when there are hundreds of thousands of them).  A different draw from
+    ``make_inputs`` with the same seed; rows past each sequence are NaN."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(lens)
+    S = int(smax if smax is not None else max(cfg.smax, int(lens.max(initial=0))))
+    if lens.size and (lens.min() < 0 or lens.max() > S):
+        raise ValueError("seq_lens must lie in [0, Smax]")
+    q = f32_to_bf16_bits(rng.standard_normal(B * cfg.Hq * cfg.D, dtype=np.float32))
+    q = q.reshape(B, cfg.Hq, cfg.D)
+    # flat row index of every valid row, (b, head) blocks of S rows in order
+    per = np.repeat(lens.astype(np.int64), cfg.Hkv)                    # rows per (b, head)
+    n = int(per.sum())
+    first = np.repeat(np.arange(B * cfg.Hkv, dtype=np.int64) * S, per)
+    within = np.arange(n, dtype=np.int64) - np.repeat(np.cumsum(per) - per, per)
+    rows = first + within
+    out = []
+    for mult in (cfg.k_mult, 1.0):
+        t = np.full((B * cfg.Hkv * S, cfg.D), BF16_QNAN, dtype=np.uint16)
+        bits = f32_to_bf16_bits(rng.standard_normal(n * cfg.D, dtype=np.float32))
+        t[rows] = _scale_bits(bits, mult).reshape(n, cfg.D)
+        out.append(t.reshape(B, cfg.Hkv, S, cfg.D))
+    return Inputs(cfg, seed, q, out[0], out[1], lens, cfg.scale)
+
+
 def config_inputs(index: int) -> Inputs:
     """The named config ``index`` at its full size, seed 42 + index."""
     return make_inputs(CONFIGS[index], 42 + index)
