@@ -56,6 +56,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -227,7 +228,6 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, int v
 }
 
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
   const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, DAS_KV_CACHE_POLICY);
   return make_uint2(v[0], v[1]);
 }
@@ -1523,16 +1523,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_attn_states_kernel(MergeA
       la[u] = a.lse_a[row];
       lb[u] = a.lse_b[row];
       const size_t base = (size_t)row * D + c;
+      // non-temporal loads and stores: the states stream through once
       if constexpr (kBf16) {
-        const uint2 ua = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.o_a) + base);
-        const uint2 ub = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.o_b) + base);
-        oa[u][0] = bf16_lo(ua.x); oa[u][1] = bf16_hi(ua.x); oa[u][2] = bf16_lo(ua.y); oa[u][3] = bf16_hi(ua.y);
-        ob[u][0] = bf16_lo(ub.x); ob[u][1] = bf16_hi(ub.x); ob[u][2] = bf16_lo(ub.y); ob[u][3] = bf16_hi(ub.y);
+        const u32x2_t ua = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(a.o_a) + base));
+        const u32x2_t ub = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(a.o_b) + base));
+        oa[u][0] = bf16_lo(ua[0]); oa[u][1] = bf16_hi(ua[0]); oa[u][2] = bf16_lo(ua[1]); oa[u][3] = bf16_hi(ua[1]);
+        ob[u][0] = bf16_lo(ub[0]); ob[u][1] = bf16_hi(ub[0]); ob[u][2] = bf16_lo(ub[1]); ob[u][3] = bf16_hi(ub[1]);
       } else {
-        const float4 fa = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.o_a) + base);
-        const float4 fb = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.o_b) + base);
-        oa[u][0] = fa.x; oa[u][1] = fa.y; oa[u][2] = fa.z; oa[u][3] = fa.w;
-        ob[u][0] = fb.x; ob[u][1] = fb.y; ob[u][2] = fb.z; ob[u][3] = fb.w;
+        const f32x4_t fa = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.o_a) + base));
+        const f32x4_t fb = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(a.o_b) + base));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          oa[u][i] = fa[i];
+          ob[u][i] = fb[i];
+        }
       }
     }
 #pragma unroll
@@ -1556,12 +1564,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_attn_states_kernel(MergeA
       }
       const size_t base = (size_t)row * D + c;
       if constexpr (kBf16) {
-        const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o_out) + base) = make_uint2(lo, hi);
+        const u32x2_t w = {f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                           f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16)};
+        __builtin_nontemporal_store(
+            w, reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.o_out) + base));
       } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o_out) + base) =
-            make_float4(v[0], v[1], v[2], v[3]);
+        const f32x4_t w = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(
+            w, reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o_out) + base));
       }
       if (c == 0) a.lse_out[row] = lse;
     }
