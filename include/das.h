@@ -282,7 +282,8 @@ int das_split_kv_decode_int4(const void* q, const void* k_cache, const void* v_c
  *                   [num_pages][page_size][Hkv] (NHD), 4-byte aligned
  *                   (k_scale/v_scale are ignored for DAS_BF16)
  *   block_table     device int32 [B][max_blocks]; entries of pages a sequence
- *                   does not reach are never read; an entry outside
+ *                   does not reach may be read (never outside row b of the
+ *                   table) but are never used; an entry outside
  *                   [0, num_pages) is clamped into it on the device (wrong
  *                   rows, never an access outside the pool)
  *   page_size       a power of two, 32 ... 65536 rows (DAS_ENOTSUP otherwise)
