@@ -184,6 +184,86 @@ def test_graph_capture_replays_match_eager():
     note("graph replays match eager")
 
 
+def _replays_match(run, outs, what):
+    """Capture run() (which writes into the tensors `outs`) in a HIP graph
+    after one eager call, replay it several times with eager work between the
+    replays, and check every replay against the eager result, bit for bit."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(outs, eager):
+            assert torch.equal(t, e), f"{what}: replay {i}"
+        _ = (torch.ones(1000, device=dev()) * 2).sum().item()   # eager work between replays
+    note(f"  {what}: graph replays match eager")
+
+
+def test_graph_capture_of_the_other_entry_points():
+    """Paged INT4 and E4M3 calls (fused merge and the separate merge kernel),
+    the no-allocation entry point and merge_attn_states, each captured in a
+    HIP graph and replayed."""
+    from test_gpu_paged import upload_paged
+
+    # paged INT4, small batch: fused merge
+    cfg = workloads.custom_config(3, 32, 8, 128, 3000, k_mult=2.0)
+    x = workloads.make_paged_inputs(cfg, 9300, 64, workloads.PAGED_HND, seq_lens=(3000, 1700, 5),
+                                    int4=True)
+    q, kp, vp, bt, sl, ks, vs = upload_paged(x)
+    out = torch.empty((3, 32, 128), device=dev())
+    lse = torch.empty((3, 32), device=dev())
+    smax = x.block_table.shape[1] * x.page_size
+    ws = torch.zeros(max(das.das_decode_workspace_bytes(3, 32, 8, smax, 128), 16),
+                     dtype=torch.uint8, device=dev())
+    _replays_match(lambda: das.das_decode_attention_paged(
+        q, kp, vp, bt, sl, x.base.scale, x.page_size, x.layout, k_scale=ks, v_scale=vs, out=out,
+        lse_out=lse, workspace=ws, kv_dtype=das.DAS_INT4), (out, lse), "paged INT4, fused merge")
+
+    # E4M3 pool, B=64: the separate merge kernel
+    rng = np.random.Generator(np.random.PCG64(9301))
+    lens = rng.integers(1, 2048, size=64, endpoint=True)
+    cfg = workloads.custom_config(64, 32, 8, 128, 2048)
+    x = workloads.make_paged_inputs(cfg, 9302, 64, workloads.PAGED_NHD, seq_lens=lens, fp8=True)
+    q, kp, vp, bt, sl, ks, vs = upload_paged(x)
+    out = torch.empty((64, 32, 128), device=dev())
+    lse = torch.empty((64, 32), device=dev())
+    smax = x.block_table.shape[1] * x.page_size
+    ws = torch.zeros(max(das.das_decode_workspace_bytes(64, 32, 8, smax, 128), 16),
+                     dtype=torch.uint8, device=dev())
+    _replays_match(lambda: das.das_decode_attention_paged(
+        q, kp, vp, bt, sl, x.base.scale, x.page_size, x.layout, k_scale=ks, v_scale=vs, out=out,
+        lse_out=lse, workspace=ws), (out, lse), "paged E4M3, separate merge kernel")
+
+    # the no-allocation entry point
+    cfg = workloads.custom_config(2, 16, 4, 128, 5000)
+    x = workloads.make_inputs(cfg, 9303, seq_lens=(5000, 2222))
+    q, k, v, sl = upload(x)
+    out = torch.empty((2, 16, 128), device=dev())
+    lse = torch.empty((2, 16), device=dev())
+    _replays_match(lambda: das.das_decode_attention_noalloc(q, k, v, sl, x.scale, out=out,
+                                                            lse_out=lse),
+                   (out, lse), "no-allocation entry point")
+
+    # merge_attn_states
+    o, sv = _states(777, 128, 9304)
+    ta = [torch.from_numpy(t).to(dev()) for t in o]
+    ts = [torch.from_numpy(t).to(dev()) for t in sv]
+    mo = torch.empty_like(ta[0])
+    ml = torch.empty_like(ts[0])
+    _replays_match(lambda: das.das_merge_attn_states(ta[0], ts[0], ta[1], ts[1], o_out=mo,
+                                                     lse_out=ml), (mo, ml), "merge_attn_states")
+
+
 def test_many_split_workgroups_take_the_two_kernel_merge():
     """B*Hkv*NS above 4 workgroups per CU: das_decode_attention merges with a
     second kernel instead of the fused last-workgroup merge; same results."""
