@@ -81,6 +81,16 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum; v_maximum3_f32, which
+// also takes a third operand).  fmaxf ignores a quiet NaN, so in the
+// kernels' IEEE mode the compiler first quiets (canonicalises) each operand
+// it cannot prove canonical -- every cross-lane value -- at one extra VALU
+// instruction per operand.  The running maxima here only ever see finite
+// logits and -inf (masked rows); a NaN input makes the output NaN either way.
+__device__ __forceinline__ float fmax_prop(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
   uint16_t u;
@@ -94,7 +104,7 @@ __device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (
 // of the row (quad swaps, then half-row and row mirrors pair the halves).
 template <bool kMax>
 __device__ __forceinline__ float row_reduce16(float x) {
-  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  auto op = [](float u, float v) { return kMax ? fmax_prop(u, v) : u + v; };
   x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
   x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
   x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
@@ -110,7 +120,7 @@ __device__ __forceinline__ float row_reduce16(float x) {
 template <int kLoBit, bool kMax>
 __device__ __forceinline__ float reduce_lane_bits(float x) {
   static_assert(kLoBit >= 3 && kLoBit <= 6, "lane bits 3..5");
-  auto op = [](float u, float v) { return kMax ? fmaxf(u, v) : u + v; };
+  auto op = [](float u, float v) { return kMax ? fmax_prop(u, v) : u + v; };
   if constexpr (kLoBit <= 5) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                     false, false);
@@ -867,7 +877,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       float x[2][4];
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        // INT4: the products start from -8 sum(q), so the sum comes out as
+        // q.(u - 8) = q.u - 8 sum(q)
+        f32x4_t sacc = kInt4 ? f32x4_t{-q8[0], -q8[0], -q8[0], -q8[0]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < kKBlocks; ++kb) {
           uint4 kw;
@@ -880,13 +892,12 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qa[kb], sacc, 0, 0, 0);
         }
         if constexpr (kInt4) {
-          // q.(u - 8) = q.u - 8 sum(q), times the row's K scale (which carries
-          // the logit scale)
+          // q.(u - 8) times the row's K scale (which carries the logit scale)
           ksc[tg] = *reinterpret_cast<const float4*>(sct + 16 * tg + 4 * grp);
-          x[tg][0] = (sacc[0] - q8[0]) * ksc[tg].x;
-          x[tg][1] = (sacc[1] - q8[0]) * ksc[tg].y;
-          x[tg][2] = (sacc[2] - q8[0]) * ksc[tg].z;
-          x[tg][3] = (sacc[3] - q8[0]) * ksc[tg].w;
+          x[tg][0] = sacc[0] * ksc[tg].x;
+          x[tg][1] = sacc[1] * ksc[tg].y;
+          x[tg][2] = sacc[2] * ksc[tg].z;
+          x[tg][3] = sacc[3] * ksc[tg].w;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[tg][r] = sacc[r] * c2;
@@ -901,8 +912,9 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       }
       // tile max of head n over the four lanes that hold it (row r0 is always
       // valid, so the max is finite)
-      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      float mt = fmax_prop(fmax_prop(fmax_prop(x[0][0], x[0][1]), x[0][2]),
+                           fmax_prop(fmax_prop(x[0][3], x[1][0]), x[1][1]));
+      mt = fmax_prop(fmax_prop(mt, x[1][2]), x[1][3]);
       mt = reduce_lane_bits<4, true>(mt);
       // Lazy rescaling: the running max moves only when a tile's max exceeds
       // it by more than kLazyLog2 (base-2 units).  Until then p = exp2(x - m)
@@ -912,7 +924,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       // by rounding.  The first tile always moves it (m starts at -inf).
       constexpr float kLazyLog2 = 8.f;
       if (__builtin_amdgcn_ballot_w64(mt > m_lane + kLazyLog2) != 0) {
-        const float mn = fmaxf(m_lane, mt);
+        const float mn = fmax_prop(m_lane, mt);
         const float alpha = fast_exp2(m_lane - mn);   // 0 on the first tile
         l_sum *= alpha;
         // row r of this lane's accumulators is head 4*grp + r, whose factor
@@ -935,12 +947,11 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
       // p in the A operand's k-slot order: slot i of lane group grp is row
       // 16*(i/4) + 4*grp + i%4 (the V operand below uses the same order)
       float pv[8];
-      float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = fast_exp2(x[i / 4][i % 4] - m_lane);
-        lsum += pv[i];
-      }
+      for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(x[i / 4][i % 4] - m_lane);
+      float lsum = pv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) lsum += pv[i];
       l_sum += lsum;
       if constexpr (kInt4) {
         // p times the row's V scale (rows past the sequence have scale 0 and p 0)
@@ -1014,8 +1025,8 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
         x[h] = ok ? x[h] * c2 : -INFINITY;
         const float mt = row_reduce16<true>(x[h]);
         float tile_max = lane_value(mt, 0);
-        if constexpr (kT == 32) tile_max = fmaxf(tile_max, lane_value(mt, 16));
-        const float mn = fmaxf(m_run[h], tile_max);
+        if constexpr (kT == 32) tile_max = fmax_prop(tile_max, lane_value(mt, 16));
+        const float mn = fmax_prop(m_run[h], tile_max);
         grow |= mn > m_run[h];
         alpha[h] = fast_exp2(m_run[h] - mn);
         m_run[h] = mn;
@@ -1297,7 +1308,7 @@ __global__ __launch_bounds__(kThreads, (min_waves_per_eu<G, kKv>()))
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    unsigned int* cnt = a.counters + (size_t)b * a.Hkv + g;
+    unsigned int* cnt = a.counters + counter_slot(b * a.Hkv + g);
     const unsigned int prev = atomicAdd(cnt, 1u);
     const bool last = prev == (unsigned int)(nsb - 1);
     if (last) atomicExch(cnt, 0u);  // leave the counter at zero for the next call
