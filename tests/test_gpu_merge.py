@@ -157,6 +157,31 @@ def test_fused_merge_leaves_counters_zero_and_repeats_exactly():
     check_f32(*first, *ref, "fused merge, forced 7 splits")
 
 
+def test_fused_merge_over_many_counter_slots():
+    """512 (b, kv-head) pairs merged in one launch (B = 64, 2 splits: 4 split
+    workgroups per CU, the most the fused call takes), each with its own
+    arrival counter on its own cache line: every pair's output matches the
+    oracle, a repeat is bitwise equal, and every counter is back at zero."""
+    cfg = workloads.custom_config(64, 32, 8, 128, 512)
+    rng = np.random.Generator(np.random.PCG64(7100))
+    lens = rng.integers(1, 512, size=64, endpoint=True)
+    x = workloads.make_inputs(cfg, 7101, seq_lens=lens)
+    q, k, v, sl = upload(x)
+    ns, _ = das.das_plan(64, 8, 4, 512, 128, 2)
+    assert ns == 2
+    assert 64 * 8 * ns <= 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    need = das.das_decode_workspace_bytes(64, 32, 8, 512, 128, ns)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    note("case fused merge, B=64 x Hkv=8 pairs, 2 splits")
+    first = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns, workspace=ws)
+    again = das.das_decode_attention(q, k, v, sl, x.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1])
+    assert int(torch.count_nonzero(ws[:das.DAS_WORKSPACE_COUNTER_BYTES])) == 0
+    check_f32(*first, *oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale),
+              "fused merge over 512 pairs")
+
+
 def test_graph_capture_replays_match_eager():
     cfg = workloads.custom_config(4, 32, 8, 128, 4096)
     x = workloads.make_inputs(cfg, 9, seq_lens=(4096, 1000, 1, 3000))
