@@ -151,6 +151,39 @@ def test_large_batch_many_split_workgroups():
     check_f32(out, lse, *ref, f"B={B} ns=2")
 
 
+def test_million_token_sequence():
+    """One sequence of 1,000,003 rows (Hq = 8, Hkv = 2, D = 64): the automatic
+    plan's chunk reaches its 8,192-row cap, so the call runs over a hundred
+    splits per kv-head, all merged in the launch by the last split to arrive,
+    and the last split ends in a ragged tile.  Against the oracle, bf16 and
+    INT4 caches; split invariance against one split."""
+    L = 1_000_003
+    cfg = workloads.custom_config(1, 8, 2, 64, L)
+    x = workloads.make_inputs(cfg, 4400)
+    ns, chunk = das.das_plan(1, 2, 4, L, 64, 0)
+    note(f"case million-token sequence: plan ns={ns} chunk={chunk}")
+    assert chunk == 8192 and ns >= 100
+    ref = oracle.attention(x.q, x.k, x.v, x.seq_lens, x.scale)
+    t = upload(x)
+    out, lse = run(x, tensors=t)
+    check_f32(out, lse, *ref, f"L={L} auto")
+    one = run(x, 1, tensors=t)
+    check_f32(*one, *ref, f"L={L} one split")
+    del t
+    y = workloads.make_int4_inputs(cfg, 4401)
+    dv = torch.device("cuda:0")
+    q = to_dev(y.q)
+    k, v = torch.from_numpy(y.k).to(dv), torch.from_numpy(y.v).to(dv)
+    ks, vs = torch.from_numpy(y.k_scale).to(dv), torch.from_numpy(y.v_scale).to(dv)
+    sl = torch.from_numpy(y.seq_lens).to(dv)
+    o4, l4 = das.das_decode_attention_int4(q, k, v, ks, vs, sl, y.scale)
+    torch.cuda.synchronize()
+    check_f32(o4, l4, *oracle.attention_int4(y.q, y.k, y.v, y.k_scale, y.v_scale, y.seq_lens,
+                                             y.scale), f"INT4 L={L} auto")
+    del q, k, v, ks, vs, sl, o4, l4
+    torch.cuda.empty_cache()
+
+
 def _steer_keys(x, ramps):
     """Give every (batch row, kv-head) a designed logit profile along the
     sequence: valid row j of K becomes a quarter of its random value plus
