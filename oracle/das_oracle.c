@@ -21,7 +21,8 @@
  *           join partial attention results through an online-softmax merge
  *           that needs each part's softmax log-sum-exp.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent (the plainest one the rest of the
+ * pages supports):
  *   - lse is the natural log of the sum of exp(scaled logit);
  *   - no epsilon is added to the softmax denominator (the emulator in §5 adds
  *     one, but the pages call the result exact, and the denominator is >= 1);
