@@ -151,6 +151,74 @@ def test_large_batch_many_split_workgroups():
     check_f32(out, lse, *ref, f"B={B} ns=2")
 
 
+def _int4_rows(codes, scales):
+    """Dequantised INT4 rows (two's-complement nibbles, element 2i low) in fp64."""
+    lo = (codes & 15).astype(np.int16)
+    hi = (codes >> 4).astype(np.int16)
+    n = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.int16)
+    n[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    n[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return n.astype(np.float64) * scales[..., None].astype(np.float64)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int4"])
+def test_closed_forms(kind):
+    """Checks that need no oracle: with every logit zero (a zero softmax
+    scale) the output is the plain mean of the sequence's V rows and the LSE
+    is ln L, over the automatic plan and forced split counts; a one-row
+    sequence returns its V row (p = 1): bit for bit from a bf16 cache (fp32
+    and bf16 output), and from an INT4 cache to within the 2^-16 relative
+    error of carrying the row's V scale as two bf16 halves."""
+    lens = (5000, 1, 777, 64)
+    cfg = workloads.custom_config(len(lens), 16, 4, 128, 5000)
+    dv = torch.device("cuda:0")
+    if kind == "bf16":
+        x = workloads.make_inputs(cfg, 4500, seq_lens=lens)
+        q, k, v, sl = upload(x)
+        rows = lambda b, g, L: workloads.bf16_bits_to_f32(x.v[b, g, :L]).astype(np.float64)
+        call = lambda scale, ns, od: das.das_decode_attention(q, k, v, sl, scale, out_dtype=od,
+                                                              num_splits=ns)
+    else:
+        x = workloads.make_int4_inputs(cfg, 4501, seq_lens=lens)
+        q = to_dev(x.q)
+        k, v = torch.from_numpy(x.k).to(dv), torch.from_numpy(x.v).to(dv)
+        ks, vs = torch.from_numpy(x.k_scale).to(dv), torch.from_numpy(x.v_scale).to(dv)
+        sl = torch.from_numpy(x.seq_lens).to(dv)
+        rows = lambda b, g, L: _int4_rows(x.v[b, g, :L], x.v_scale[b, g, :L])
+        call = lambda scale, ns, od: das.das_decode_attention_int4(
+            q, k, v, ks, vs, sl, scale, out_dtype=od, num_splits=ns)
+    B, Hq, D = x.q.shape
+    Hkv = x.k.shape[1]
+    G = Hq // Hkv
+    want = np.zeros((B, Hq, D))
+    for b, L in enumerate(lens):
+        for h in range(Hq):
+            want[b, h] = rows(b, h // G, L).mean(axis=0)
+    want_l = np.repeat(np.log(np.asarray(lens, dtype=np.float64))[:, None], Hq, axis=1)
+    for ns in (0, 1, 3, 9):
+        note(f"case closed form {kind}: zero scale, num_splits={ns}")
+        out, lse = call(0.0, ns, torch.float32)
+        torch.cuda.synchronize()
+        check_f32(out, lse, want, want_l, f"{kind} zero scale ns={ns}")
+    # the one-row sequence (b = 1), at the workload's own scale
+    for od in (torch.float32, torch.bfloat16):
+        out, _ = call(x.scale, 0, od)
+        torch.cuda.synchronize()
+        got = out[1].float().cpu().numpy().astype(np.float64)
+        for h in range(Hq):
+            row = rows(1, h // G, 1)[0]
+            if kind == "int4":
+                if od == torch.float32:
+                    assert np.all(np.abs(got[h] - row) <= 2.0 ** -16 * np.abs(row)), \
+                        f"int4: one-row sequence, head {h}: not its V row"
+                continue
+            if od == torch.bfloat16:
+                row = workloads.bf16_bits_to_f32(
+                    workloads.f32_to_bf16_bits(row.astype(np.float32))).astype(np.float64)
+            assert np.array_equal(got[h], row.astype(np.float32).astype(np.float64)), \
+                f"bf16: one-row sequence, head {h}, {od}: not its V row"
+
+
 def test_million_token_sequence():
     """One sequence of 1,000,003 rows (Hq = 8, Hkv = 2, D = 64): the automatic
     plan's chunk reaches its 8,192-row cap, so the call runs over a hundred
